@@ -1,0 +1,269 @@
+"""Seeded synthetic workloads for ring attention on one device's share.
+
+This module only builds inputs: random values, bf16 rounding of those inputs,
+and the position / ring-order bookkeeping of a share. It holds none of the
+method's arithmetic, so both the HIP path and the fp64 oracle consume what it
+produces without sharing any code with each other.
+
+Positions follow "Ring Attention: Distributed Reads with Online Softmax":
+a sequence of ``n`` tokens is cut into ``P`` shards (section "Partition the
+sequence across devices"); the device at ring index ``r`` meets, at step
+``s``, the shard of device ``(r - s) mod P`` (it receives from its
+predecessor), so the chunk list below is in that ring order. Section "Causal
+masks depend on global positions" gives the two causal layouts used here:
+contiguous shards and paired early/late chunks ("zigzag": with ``2P`` chunks,
+device ``r`` owns chunks ``r`` and ``2P-1-r``).
+
+Values: q, k, v are standard normal fp32, drawn per block of global positions
+from ``numpy.random.default_rng([seed, tensor, block])`` so that any re-split of
+the same positions sees identical values; bf16 workloads round them to bf16
+(round to nearest even) before either side sees them.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+POS_BLOCK = 4096  # positions per seeded block
+
+
+@dataclasses.dataclass
+class Workload:
+    """One device's share: local queries and the K/V chunks it meets, in ring order."""
+
+    name: str
+    dtype: str  # "f32" or "bf16"
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    q_segments: List[Tuple[int, int]]  # (global_offset, length) per run of local query rows
+    chunks: List[Tuple[int, int]]  # (global_offset, length) per K/V chunk, list order = ring order
+    causal: bool
+    seq_len: int  # n: positions 0..n-1 hold keys
+    q_std: float = 1.0
+    seed: int = 0
+    scale: Optional[float] = None  # None means 1/sqrt(head_dim)
+
+    @property
+    def lq(self) -> int:
+        return sum(n for _, n in self.q_segments)
+
+    @property
+    def lk(self) -> int:
+        return sum(n for _, n in self.chunks)
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / float(np.sqrt(self.head_dim))
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 value (ties to even); result stays fp32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + r) & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+def ring_order(rank: int, world: int) -> List[int]:
+    """Shard seen at each ring step by device ``rank``: ``(rank - step) mod world``."""
+    return [(rank - s) % world for s in range(world)]
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+
+
+def scalar_case() -> dict:
+    """Two single-key shards: A has score 0 and value 0, B has score 10 and value 1.
+
+    From section "Do not average independently normalized shard outputs": with
+    d = 1, scale 1 and q = 1 the scores are the keys themselves.
+    """
+    return {
+        "q": np.ones((1, 1, 1, 1), np.float32),
+        "k": [np.zeros((1, 1, 1, 1), np.float32), np.full((1, 1, 1, 1), 10.0, np.float32)],
+        "v": [np.zeros((1, 1, 1, 1), np.float32), np.ones((1, 1, 1, 1), np.float32)],
+        "kv_offsets": [0, 1],
+        "q_positions": [1],
+        "scale": 1.0,
+    }
+
+
+def tiny(causal: bool = False) -> Workload:
+    """fp32, 1 head, d=16, 8 queries, 32 keys in chunks [1, 3, 12, 16]; causal queries at 24..31."""
+    return Workload("tiny_f32" + ("_causal" if causal else ""), "f32", 1, 1, 1, 16,
+                    [(24, 8)], [(0, 1), (1, 3), (4, 12), (16, 16)], causal, 32, seed=100)
+
+
+def noncausal_d64() -> Workload:
+    """bf16, 8 heads, d=64, 4096 local queries (device 0 of 8) vs 8 shards of 4096."""
+    P, L = 8, 4096
+    return Workload("noncausal_h8_d64_q4k_k32k", "bf16", 1, 8, 8, 64, [(0, L)],
+                    [(j * L, L) for j in ring_order(0, P)], False, P * L, seed=101)
+
+
+def causal_contiguous() -> Workload:
+    """bf16, 32 heads, d=128, device 5 of 8, n=65536: 8192 queries at 40960..49151."""
+    P, L, r = 8, 8192, 5
+    return Workload("causal_contig_r5of8_h32_d128_n64k", "bf16", 1, 32, 32, 128, [(r * L, L)],
+                    [(j * L, L) for j in ring_order(r, P)], True, P * L, seed=102)
+
+
+def causal_zigzag() -> Workload:
+    """bf16, 32 heads, d=128, device 3 of 16, n=131072 in 32 chunks of 4096.
+
+    The local share is chunks 3 and 28; shard ``j`` is chunks ``j`` and ``31-j``,
+    passed as two chunk descriptors each.
+    """
+    P, C, r = 16, 4096, 3
+    chunks = []
+    for j in ring_order(r, P):
+        chunks += [(j * C, C), ((2 * P - 1 - j) * C, C)]
+    return Workload("causal_zigzag_r3of16_h32_d128_n128k", "bf16", 1, 32, 32, 128,
+                    [(r * C, C), ((2 * P - 1 - r) * C, C)], chunks, True, 2 * P * C, seed=103)
+
+
+def long_gqa() -> Workload:
+    """bf16 GQA, 8 query heads on 1 KV head, d=128, 16384 queries vs 64 shards of 16384."""
+    P, L = 64, 16384
+    return Workload("long_gqa_hq8_hkv1_d128_q16k_k1m", "bf16", 1, 8, 1, 128, [(0, L)],
+                    [(j * L, L) for j in ring_order(0, P)], False, P * L, q_std=4.0, seed=104)
+
+
+CONFIGS = {0: tiny, 1: noncausal_d64, 2: causal_contiguous, 3: causal_zigzag, 4: long_gqa}
+
+
+def config(i: int, **kw) -> Workload:
+    return CONFIGS[i](**kw)
+
+
+def custom(name, dtype, batch, q_heads, kv_heads, head_dim, q_segments, chunks, causal,
+           seq_len=None, q_std=1.0, seed=7, scale=None) -> Workload:
+    if seq_len is None:
+        seq_len = max([o + n for o, n in chunks] + [o + n for o, n in q_segments] + [0])
+    return Workload(name, dtype, batch, q_heads, kv_heads, head_dim, list(q_segments), list(chunks),
+                    causal, seq_len, q_std, seed, scale)
+
+
+def resplit(w: Workload, cuts: Sequence[int]) -> Workload:
+    """The same ordered key sequence cut into chunks at other places.
+
+    ``cuts`` are indices into the concatenated key list. Adjacent chunks whose
+    positions continue each other are first joined; the joined runs are then cut
+    at ``cuts``. Every key keeps its place and its global position, so the data
+    and the exact result are unchanged.
+    """
+    runs = []
+    for o, n in w.chunks:
+        if n == 0:
+            continue
+        if runs and runs[-1][0] + runs[-1][1] == o:
+            runs[-1] = (runs[-1][0], runs[-1][1] + n)
+        else:
+            runs.append((o, n))
+    bounds = sorted(set(int(c) for c in cuts if 0 < int(c) < w.lk))
+    out, s0 = [], 0
+    for o, n in runs:
+        inner = [c - s0 for c in bounds if s0 < c < s0 + n]
+        edges = [0] + inner + [n]
+        out += [(o + a, b - a) for a, b in zip(edges[:-1], edges[1:])]
+        s0 += n
+    return dataclasses.replace(w, chunks=out, name=w.name + "_resplit")
+
+
+# ---------------------------------------------------------------------------
+# value generation
+
+
+def _normal_positions(seed: int, tensor: int, lead: Tuple[int, ...], start: int, stop: int,
+                      d: int) -> np.ndarray:
+    """Standard normals for positions [start, stop), seeded per block of POS_BLOCK positions."""
+    out = np.empty(lead + (max(stop - start, 0), d), dtype=np.float32)
+    if stop <= start:
+        return out
+    for blk in range(start // POS_BLOCK, (stop - 1) // POS_BLOCK + 1):
+        g = np.random.default_rng([seed, tensor, blk])
+        vals = g.standard_normal(lead + (POS_BLOCK, d), dtype=np.float32)
+        lo, hi = max(start, blk * POS_BLOCK), min(stop, (blk + 1) * POS_BLOCK)
+        out[..., lo - start:hi - start, :] = vals[..., lo - blk * POS_BLOCK:hi - blk * POS_BLOCK, :]
+    return out
+
+
+def generate_numpy(w: Workload):
+    """Host inputs: q [B,Hq,Lq,d] and full k, v [B,Hkv,n,d] over global positions (fp32 arrays).
+
+    bf16 workloads hold bf16-representable values. Chunk ``c`` of the ring list
+    is ``k[:, :, o:o+len]`` with ``(o, len) = w.chunks[c]``.
+    """
+    B, Hq, Hkv, d = w.batch, w.q_heads, w.kv_heads, w.head_dim
+    q = np.concatenate([_normal_positions(w.seed, 0, (B, Hq), o, o + n, d) for o, n in w.q_segments],
+                       axis=2) if w.q_segments else np.zeros((B, Hq, 0, d), np.float32)
+    if w.q_std != 1.0:
+        q = q * np.float32(w.q_std)
+    k = _normal_positions(w.seed, 1, (B, Hkv), 0, w.seq_len, d)
+    v = _normal_positions(w.seed, 2, (B, Hkv), 0, w.seq_len, d)
+    if w.dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return q, k, v
+
+
+def generate_torch(w: Workload, device="cpu"):
+    """The same inputs as torch tensors (bf16 or fp32) on ``device``.
+
+    Returns ``(q, k_full, v_full, key_chunks, value_chunks)``; the chunk lists
+    are views into ``k_full``/``v_full`` in ring order, so no data is copied.
+    """
+    import torch
+
+    q, k, v = generate_numpy(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tq = torch.from_numpy(q).to(device=device).to(tdt)
+    tk = torch.from_numpy(k).to(device=device).to(tdt)
+    tv = torch.from_numpy(v).to(device=device).to(tdt)
+    kc = [tk[:, :, o:o + n] for o, n in w.chunks]
+    vc = [tv[:, :, o:o + n] for o, n in w.chunks]
+    return tq, tk, tv, kc, vc
+
+
+# ---------------------------------------------------------------------------
+# bookkeeping used by the benchmark and by sampled checks
+
+
+def q_positions(w: Workload) -> np.ndarray:
+    parts = [np.arange(n, dtype=np.int64) + o for o, n in w.q_segments]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
+def unmasked_pairs_per_head(w: Workload) -> int:
+    """Number of (query, key) pairs the mask allows, per query head and batch entry."""
+    if not w.causal:
+        return w.lq * w.lk
+    kpos = np.sort(np.concatenate([np.arange(n, dtype=np.int64) + o for o, n in w.chunks]))
+    return int(np.searchsorted(kpos, q_positions(w), side="right").sum())
+
+
+def counted_flops(w: Workload) -> int:
+    """4 * d flops per allowed (query, key) pair per query head: two matmuls of 2*d each."""
+    return 4 * w.head_dim * w.q_heads * w.batch * unmasked_pairs_per_head(w)
+
+
+def sample_rows(w: Workload, count: int, seed: int = 0, tile: int = 128) -> List[Tuple[int, int, int]]:
+    """Stratified ``(b, h, row)`` sample: segment ends, tile edges, then seeded random rows."""
+    g = np.random.default_rng([seed, 991])
+    picks = []
+    starts = np.cumsum([0] + [n for _, n in w.q_segments])
+    special = set()
+    for s0, s1 in zip(starts[:-1], starts[1:]):
+        if s1 > s0:
+            special.update([int(s0), int(s1) - 1])
+    for t in range(tile, w.lq, tile * 7):
+        special.update([t - 1, t])
+    for i, r in enumerate(sorted(special)):
+        picks.append((i % w.batch, (i * 5) % w.q_heads, r))
+    while len(picks) < count:
+        picks.append((int(g.integers(w.batch)), int(g.integers(w.q_heads)), int(g.integers(w.lq))))
+    return picks[:max(count, 0)] if count < len(picks) else picks
