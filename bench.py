@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring-attention hot path on one MI355X.
+
+One step is one ``ring_attention`` call over one device's full share (every
+key/value chunk, in ring order, with the causal mask if the workload has one),
+with inputs already resident in HBM. The JSON line reports the counted
+throughput ``4 * d * Hq * (allowed query-key pairs)`` per second, the roofline
+of the attention kernel (bf16 MFMA bound), the standalone chunk-statistics and
+merge legs (the merge is HBM-bound, next to a device copy of the same size),
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+KERNEL_SOURCE = os.path.join(ROOT, "ring_attention_chunk_amd", "csrc", "attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1 is the reported workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true", help="skip the chunk-stats and merge legs")
+    return ap.parse_args()
+
+
+def source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per call
+
+
+def traffic_for(workload_name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    path = os.path.join(ROOT, "profiles", f"attention_kernel_{workload_name}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256_16") != source_digest():
+        return None  # the kernel changed since the counters were taken
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, kc, vc, offs, seconds):
+    """The fp64 oracle on host cores over whole row blocks of the same share, for ~`seconds`."""
+    import numpy as np
+
+    import oracle
+    from ring_attention_chunk_amd import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = 1
+    qpos = wl.q_positions(w)
+    qh = q.cpu()
+    kh = [c.cpu() for c in kc]
+    vh = [c.cpu() for c in vc]
+    block = 256
+    flops, rows, t0 = 0, 0, time.perf_counter()
+    kpos = np.sort(np.concatenate([np.arange(n) + o for o, n in w.chunks]))
+    h = 0
+    r0 = 0
+    while time.perf_counter() - t0 < seconds:
+        r1 = min(w.lq, r0 + block)
+        oracle.attention(qh[:, h:h + 1, r0:r1], [c[:, (h * w.kv_heads) // w.q_heads:][:, :1] for c in kh],
+                         [c[:, (h * w.kv_heads) // w.q_heads:][:, :1] for c in vh], qpos[r0:r1], offs,
+                         causal=w.causal, scale=w.softmax_scale)
+        pairs = (r1 - r0) * w.lk if not w.causal else int(np.searchsorted(kpos, qpos[r0:r1], side="right").sum())
+        flops += 4 * w.head_dim * pairs * w.batch
+        rows += (r1 - r0) * w.batch
+        r0 = r1
+        if r0 >= w.lq:
+            r0, h = 0, (h + 1) % w.q_heads
+    wall = time.perf_counter() - t0
+    return {
+        "value": flops / wall / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{rows} query rows (blocks of {block} rows, head by head, every key) of {w.name}; "
+                  f"{wall:.1f} s wall; numpy fp64 on {platform.processor() or platform.machine()}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the whole share on a single MI355X and has no "
+              "multi-GPU path; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ring_attention_chunk_amd as ra
+    from ring_attention_chunk_amd import workloads as wl
+
+    ra.load_library()
+    dev = "cuda:0"
+    w = wl.config(args.config)
+    q, k, v, kc, vc = wl.generate_torch(w, dev)
+    offs = [o for o, _ in w.chunks]
+    flops = wl.counted_flops(w)
+    ws = torch.empty(ra.api.load_library().ra_ring_workspace_bytes(len(kc), len(w.q_segments)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, scale=w.softmax_scale,
+                                 workspace=ws)
+
+    ms = timed(step, args.steps, args.warmup, torch)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    traffic = traffic_for(w.name)
+    result = {
+        "metric": "ring_attention TFLOP/s at 1 GPU (counted 4*d*Hq*allowed pairs) and % of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "q_heads": w.q_heads,
+            "kv_heads": w.kv_heads,
+            "head_dim": w.head_dim,
+            "local_queries": w.lq,
+            "keys": w.lk,
+            "kv_chunks": len(w.chunks),
+            "causal": w.causal,
+            "counted_flops": flops,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": traffic,
+        },
+        "pct_of_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+        "kernel_source_sha256_16": source_digest(),
+    }
+
+    if not args.no_legs:
+        legs = {}
+        # standalone attention_chunk_stats on one shard of the share
+        k0, v0 = kc[0], vc[0]
+        ms_s = timed(lambda: ra.attention_chunk_stats(q, k0, v0, scale=w.softmax_scale), args.steps,
+                     args.warmup, torch)
+        f_s = 4 * w.head_dim * w.q_heads * w.batch * w.lq * k0.shape[2]
+        legs["attention_chunk_stats"] = {"ms": round(ms_s, 4), "TFLOP/s": round(f_s / (ms_s * 1e-3) / 1e12, 2),
+                                         "shape": f"{w.lq} queries x {k0.shape[2]} keys, {w.q_heads} heads"}
+        # standalone merge at the 32-head, d=128, 8192-row shape; 4 rotating buffer sets
+        rows, d = 32 * 8192, 128
+        sets = [(torch.randn(rows, d, device=dev), torch.rand(rows, device=dev) + 0.5,
+                 torch.randn(rows, device=dev)) for _ in range(8)]
+        it = [0]
+
+        def merge_step():
+            i = it[0]
+            it[0] = (i + 2) % 8
+            ra.merge_chunk_stats(sets[i], sets[i + 1], inplace=True)
+
+        ms_m = timed(merge_step, max(args.steps, 20), args.warmup, torch)
+        mbytes = 12 * (d + 2) * rows
+        src = torch.empty(mbytes // 8, dtype=torch.float32, device=dev)  # read + write = mbytes
+        dst = torch.empty_like(src)
+        srcs = [torch.empty_like(src) for _ in range(3)]
+        ci = [0]
+
+        def copy_step():
+            j = ci[0]
+            ci[0] = (j + 1) % 3
+            dst.copy_(srcs[j])
+
+        ms_c = timed(copy_step, max(args.steps, 20), args.warmup, torch)
+        legs["merge_chunk_stats"] = {
+            "ms": round(ms_m, 4),
+            "GB/s": round(mbytes / (ms_m * 1e-3) / 1e9, 1),
+            "bytes_per_call": mbytes,
+            "frac_of_hbm_peak": round(mbytes / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "device_copy_GB/s": round(mbytes / (ms_c * 1e-3) / 1e9, 1),
+            "shape": f"{rows} rows x d={d}, fp32, 4 rotating buffer sets",
+        }
+        del sets, src, dst, srcs
+        result["legs"] = legs
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, kc, vc, offs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

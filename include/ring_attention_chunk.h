@@ -1,0 +1,147 @@
+/*
+ * ring_attention_chunk.h -- C ABI of the MI355X (gfx950) ring-attention library.
+ *
+ * The library computes one device's share of ring attention on one GPU: the
+ * local queries attend to a list of key/value chunks that are already resident
+ * in device memory, visited in list order (the ring order). Three calls follow
+ * the exercise page "systems-distributed-ring-attention-online-softmax"
+ * (problem statement): per-chunk online-softmax statistics, the merge of two
+ * statistics, and the whole ring pass with one normalisation at the end.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All pointers to tensors are DEVICE pointers owned by the caller. The
+ *    library allocates no device memory. Host pointers (descriptor arrays)
+ *    need to stay valid only for the duration of the call.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *    default stream). A status of RA_OK means the work was enqueued; faults
+ *    inside kernels surface at the caller's next synchronisation.
+ *  - Every argument is validated on the host before any HIP call. On error a
+ *    call returns a nonzero status, enqueues nothing, and leaves a message for
+ *    ra_last_error() (per host thread). Calls never abort or print.
+ *  - Scores are s = scale * <q, k>, in natural-log units; scale must be finite
+ *    and > 0 (1/sqrt(head_dim) is the usual choice).
+ *  - Element types: RA_BF16 inputs use bf16 matrix cores with fp32
+ *    accumulation; RA_F32 inputs use fp32 matrix cores. All statistics and
+ *    outputs are fp32.
+ *  - head_dim is 1..128; q_heads must be a multiple of kv_heads (query head h
+ *    reads key/value head h / (q_heads / kv_heads)).
+ *  - Global positions (chunk offsets, query segment offsets, and offset+len)
+ *    must lie in [0, 2^31 - 2]; the total number of keys must be < 2^31.
+ *
+ * Layouts
+ * -------
+ *  q          [batch, q_heads, q_len, head_dim], contiguous, element type dtype.
+ *  chunk      per chunk: key row j of batch b, kv head h starts at element
+ *             b*stride_b + h*stride_h + j*stride_s of `k` (and of `v`, which
+ *             shares the strides); the head_dim elements of a row are
+ *             contiguous. A chunk can therefore be a slice of a larger
+ *             [batch, kv_heads, n, head_dim] buffer without a copy.
+ *  u, out     [batch, q_heads, q_len, head_dim] fp32, contiguous.
+ *  l, m, lse  [batch, q_heads, q_len] fp32, contiguous.
+ *  Output buffers must not overlap any input.
+ */
+#ifndef RING_ATTENTION_CHUNK_H
+#define RING_ATTENTION_CHUNK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ra_status {
+  RA_OK = 0,
+  RA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  RA_ERR_SHAPE = 2,       /* sizes, strides, offsets or lengths are invalid    */
+  RA_ERR_DTYPE = 3,       /* unknown element type                              */
+  RA_ERR_UNSUPPORTED = 4, /* valid request outside what the kernels implement  */
+  RA_ERR_HIP = 5,         /* the HIP runtime refused a copy or a launch        */
+  RA_ERR_WORKSPACE = 6    /* workspace missing or smaller than required        */
+};
+
+enum ra_dtype { RA_F32 = 0, RA_BF16 = 1 };
+
+/* One key/value chunk: a contiguous run of global key positions starting at
+ * global_offset ("Ring Attention: Distributed Reads with Online Softmax",
+ * section "Causal masks depend on global positions": shard metadata carries
+ * global positions). Strides are in elements; stride_s >= head_dim. */
+typedef struct ra_kv_chunk {
+  const void* k;
+  const void* v;
+  int64_t len;           /* keys in this chunk, >= 0 (0 contributes nothing) */
+  int64_t global_offset; /* global position of the chunk's first key         */
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_s;
+} ra_kv_chunk;
+
+/* A run of local query rows with consecutive global positions. A contiguous
+ * share is one segment; a paired early/late ("zigzag") share is two. */
+typedef struct ra_q_segment {
+  int64_t len;
+  int64_t global_offset;
+} ra_q_segment;
+
+/* attention_chunk_stats(query, key_chunk, value_chunk) -> (u, l, m).
+ * Exercise page, problem statement and hint 1: for every query row, the
+ * un-normalised weighted value sum u, the un-normalised softmax denominator l
+ * and the row-wise maximum score m over this one chunk, computed as if it were
+ * the only chunk (no mask). u is relative to m: u = sum_j exp(s_j - m) v_j,
+ * l = sum_j exp(s_j - m). A chunk of length 0 yields (0, 0, -inf).
+ * Writes u [B,Hq,q_len,d], l and m [B,Hq,q_len]. */
+int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, int head_dim,
+                             const void* q, int64_t q_len, const ra_kv_chunk* chunk,
+                             float scale, float* u, float* l, float* m, void* stream);
+
+/* merge_chunk_stats(acc, chunk), in place on acc.
+ * Exercise page, hint 2 ("rescale to the shared new max"): with
+ * m' = max(m_acc, m_chunk), both sides are multiplied by exp(own_max - m')
+ * before adding: l' = a l_acc + b l_chunk, u' = a u_acc + b u_chunk, m' as
+ * above. Two -inf maxima give the identity (0, 0, -inf). rows is the number of
+ * (batch, head, query) rows; u has head_dim floats per row. acc_* are read and
+ * overwritten; the chunk arrays must not overlap them. */
+int ra_merge_chunk_stats(int64_t rows, int head_dim, float* acc_u, float* acc_l, float* acc_m,
+                         const float* u, const float* l, const float* m, void* stream);
+
+/* Device workspace, in bytes, that ra_ring_attention needs for n_chunks chunk
+ * descriptors and n_q_segments query segments (a multiple of 256). */
+size_t ra_ring_workspace_bytes(int n_chunks, int n_q_segments);
+
+/* ring_attention(query, key_chunks, value_chunks, q_global_offset,
+ * kv_global_offsets, causal) -> normalised output.
+ * Exercise page, problem statement: the result equals ordinary softmax
+ * attention over the concatenation of the chunks in list order, for any split
+ * of that sequence into chunks; the blog post's "A simple forward schedule"
+ * keeps one running (m, l, u) per query across all chunks and divides u / l
+ * once at the end. With causal != 0 a key is allowed for a query when its
+ * global position is <= the query's (section "Causal masks depend on global
+ * positions"). Rows with no allowed key give out = 0 and lse = -inf.
+ *  q_segments  host array of n_q_segments runs whose lengths sum to q_len
+ *              (n_q_segments >= 1); positions matter only when causal.
+ *  chunks      host array of n_chunks descriptors in ring order (n_chunks >= 0).
+ *  workspace   device buffer of >= ra_ring_workspace_bytes(n_chunks,
+ *              n_q_segments) bytes, 256-byte aligned; the descriptor table is
+ *              copied there on `stream` (stream-ordered), so two calls on one
+ *              stream may share it, calls on different streams may not.
+ *  out         [B,Hq,q_len,d] fp32; lse [B,Hq,q_len] fp32 or NULL.
+ * For a fixed ordered key sequence the output is bit-identical for every split
+ * of that sequence into chunks and from run to run. */
+int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_dim,
+                      const void* q, const ra_q_segment* q_segments, int n_q_segments,
+                      const ra_kv_chunk* chunks, int n_chunks, int causal, float scale,
+                      void* workspace, size_t workspace_bytes, float* out, float* lse,
+                      void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* ra_status_string(int status);
+
+/* Message describing the last failed call on this host thread ("" if none). */
+const char* ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_ATTENTION_CHUNK_H */

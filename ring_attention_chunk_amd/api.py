@@ -1,0 +1,254 @@
+"""Thin Python binding of the C ABI (ctypes): argument marshalling only.
+
+Every step of the computation runs in the HIP library; this module checks
+tensor shapes, fills the C descriptor structs, allocates outputs with torch
+(device memory is torch's) and passes torch's current stream. There is no
+fallback: if the library is missing or no GPU is present, calls raise.
+
+The three calls keep the names of the exercise page
+"systems-distributed-ring-attention-online-softmax" (problem statement):
+``attention_chunk_stats``, ``merge_chunk_stats`` and ``ring_attention``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence, Tuple, Union
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libring_attention_chunk.so")
+
+RA_F32, RA_BF16 = 0, 1
+
+# exported symbols, as declared in include/ring_attention_chunk.h
+EXPORTS = (
+    "ra_attention_chunk_stats",
+    "ra_merge_chunk_stats",
+    "ra_ring_workspace_bytes",
+    "ra_ring_attention",
+    "ra_status_string",
+    "ra_last_error",
+)
+
+
+class KVChunk(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("len", ctypes.c_int64),
+        ("global_offset", ctypes.c_int64),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_s", ctypes.c_int64),
+    ]
+
+
+class QSegment(ctypes.Structure):
+    _fields_ = [("len", ctypes.c_int64), ("global_offset", ctypes.c_int64)]
+
+
+class RingAttentionError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RingAttentionError(
+            f"HIP library not found at {path}; build it with "
+            "`python -m ring_attention_chunk_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.ra_attention_chunk_stats.argtypes = [i32, i32, i32, i32, i32, vp, i64, ctypes.POINTER(KVChunk), f32,
+                                             vp, vp, vp, vp]
+    lib.ra_attention_chunk_stats.restype = i32
+    lib.ra_merge_chunk_stats.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.ra_merge_chunk_stats.restype = i32
+    lib.ra_ring_workspace_bytes.argtypes = [i32, i32]
+    lib.ra_ring_workspace_bytes.restype = sz
+    lib.ra_ring_attention.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
+                                      ctypes.POINTER(KVChunk), i32, i32, f32, vp, sz, vp, vp, vp]
+    lib.ra_ring_attention.restype = i32
+    lib.ra_status_string.argtypes = [i32]
+    lib.ra_status_string.restype = ctypes.c_char_p
+    lib.ra_last_error.argtypes = []
+    lib.ra_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(lib, status: int, what: str):
+    if status != 0:
+        msg = lib.ra_last_error().decode()
+        name = lib.ra_status_string(status).decode()
+        raise RingAttentionError(f"{what}: {name} ({status}): {msg}")
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_F32
+    raise RingAttentionError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise RingAttentionError("tensors must live on the GPU (no CPU path exists)")
+
+
+def _chunk_desc(k, v, offset: int, batch: int, kv_heads: int, head_dim: int) -> KVChunk:
+    if k.dim() != 4 or v.dim() != 4:
+        raise RingAttentionError("key/value chunks must be [batch, kv_heads, len, head_dim]")
+    if tuple(k.shape) != tuple(v.shape):
+        raise RingAttentionError(f"key chunk {tuple(k.shape)} and value chunk {tuple(v.shape)} differ")
+    if k.shape[0] != batch or k.shape[1] != kv_heads or k.shape[3] != head_dim:
+        raise RingAttentionError(f"chunk shape {tuple(k.shape)} does not match batch={batch}, "
+                                 f"kv_heads={kv_heads}, head_dim={head_dim}")
+    if k.stride() != v.stride():
+        raise RingAttentionError("key and value chunks must share strides")
+    if k.shape[2] > 0 and k.stride(3) != 1:
+        raise RingAttentionError("the head_dim axis of a chunk must be contiguous")
+    sb, sh, ss, _ = k.stride()
+    if k.shape[2] <= 1:
+        ss = max(ss, head_dim)
+    return KVChunk(k.data_ptr(), v.data_ptr(), int(k.shape[2]), int(offset), int(sb), int(sh), int(ss))
+
+
+def attention_chunk_stats(query, key_chunk, value_chunk, scale: Optional[float] = None):
+    """Statistics of one chunk: ``(u, l, m)`` (un-normalised numerator, denominator, row max).
+
+    query [B, Hq, Lq, d]; key_chunk, value_chunk [B, Hkv, Lc, d] (bf16 or fp32, on the GPU).
+    Returns fp32 tensors u [B, Hq, Lq, d], l and m [B, Hq, Lq].
+    """
+    torch = _torch()
+    lib = load_library()
+    _require_gpu(query, key_chunk, value_chunk)
+    if query.dim() != 4:
+        raise RingAttentionError("query must be [batch, q_heads, q_len, head_dim]")
+    if key_chunk.dtype != query.dtype or value_chunk.dtype != query.dtype:
+        raise RingAttentionError("query, key and value must share a dtype")
+    q = query.contiguous()
+    B, Hq, Lq, d = q.shape
+    Hkv = key_chunk.shape[1] if key_chunk.dim() == 4 else 0
+    desc = _chunk_desc(key_chunk, value_chunk, 0, B, Hkv, d)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    u = torch.empty((B, Hq, Lq, d), dtype=torch.float32, device=q.device)
+    l = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    m = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    st = lib.ra_attention_chunk_stats(_dtype_code(q), B, Hq, Hkv, d, q.data_ptr(), Lq, ctypes.byref(desc),
+                                      float(scale), u.data_ptr(), l.data_ptr(), m.data_ptr(), _stream(q))
+    _check(lib, st, "attention_chunk_stats")
+    return u, l, m
+
+
+def merge_chunk_stats(acc, chunk, inplace: bool = False):
+    """Merge ``chunk = (u, l, m)`` into ``acc = (u, l, m)`` by the rescale-to-shared-max rule.
+
+    Returns the merged triple. With ``inplace=True`` the accumulator tensors
+    are overwritten and returned; otherwise new tensors are returned.
+    """
+    lib = load_library()
+    au, al, am = acc
+    bu, bl, bm = chunk
+    _require_gpu(au, al, am, bu, bl, bm)
+    for t in (au, al, am, bu, bl, bm):
+        if t.dtype != _torch().float32:
+            raise RingAttentionError("statistics are fp32 tensors")
+    if au.shape != bu.shape or al.shape != bl.shape or am.shape != bm.shape or al.shape != am.shape:
+        raise RingAttentionError("accumulator and chunk statistics differ in shape")
+    if tuple(au.shape[:-1]) != tuple(al.shape):
+        raise RingAttentionError("u must be l's shape plus a trailing head_dim axis")
+    if not inplace:
+        au, al, am = au.clone(), al.clone(), am.clone()
+    elif not (au.is_contiguous() and al.is_contiguous() and am.is_contiguous()):
+        raise RingAttentionError("in-place merge needs contiguous accumulator tensors")
+    bu, bl, bm = bu.contiguous(), bl.contiguous(), bm.contiguous()
+    d = au.shape[-1]
+    rows = al.numel()
+    st = lib.ra_merge_chunk_stats(rows, d, au.data_ptr(), al.data_ptr(), am.data_ptr(), bu.data_ptr(),
+                                  bl.data_ptr(), bm.data_ptr(), _stream(au))
+    _check(lib, st, "merge_chunk_stats")
+    return au, al, am
+
+
+QOffset = Union[int, Sequence[Tuple[int, int]]]
+
+
+def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global_offset: QOffset = 0,
+                   kv_global_offsets: Optional[Sequence[int]] = None, causal: bool = False,
+                   scale: Optional[float] = None, return_lse: bool = False, workspace=None):
+    """Attention of the local queries over all chunks, in list (ring) order, normalised once.
+
+    ``q_global_offset`` is the global position of the first query (an int), or
+    a list of ``(global_offset, length)`` runs covering the query rows (two
+    runs for a paired early/late share). ``kv_global_offsets`` gives each
+    chunk's first global position; by default chunks follow each other from 0.
+    Returns out [B, Hq, Lq, d] fp32 (and lse [B, Hq, Lq] if ``return_lse``).
+    """
+    torch = _torch()
+    lib = load_library()
+    if len(key_chunks) != len(value_chunks):
+        raise RingAttentionError("key_chunks and value_chunks differ in length")
+    _require_gpu(query, *key_chunks, *value_chunks)
+    if query.dim() != 4:
+        raise RingAttentionError("query must be [batch, q_heads, q_len, head_dim]")
+    q = query.contiguous()
+    B, Hq, Lq, d = q.shape
+    for t in list(key_chunks) + list(value_chunks):
+        if t.dtype != q.dtype:
+            raise RingAttentionError("query, keys and values must share a dtype")
+    if kv_global_offsets is None:
+        kv_global_offsets, acc = [], 0
+        for k in key_chunks:
+            kv_global_offsets.append(acc)
+            acc += int(k.shape[2])
+    if len(kv_global_offsets) != len(key_chunks):
+        raise RingAttentionError("one global offset per chunk is required")
+    Hkv = int(key_chunks[0].shape[1]) if key_chunks else Hq
+    n = len(key_chunks)
+    descs = (KVChunk * max(n, 1))()
+    for i, (k, v, off) in enumerate(zip(key_chunks, value_chunks, kv_global_offsets)):
+        descs[i] = _chunk_desc(k, v, off, B, Hkv, d)
+    if isinstance(q_global_offset, int):
+        segs_py = [(int(q_global_offset), Lq)]
+    else:
+        segs_py = [(int(o), int(n_)) for o, n_ in q_global_offset]
+    if sum(n_ for _, n_ in segs_py) != Lq:
+        raise RingAttentionError(f"query segments cover {sum(n_ for _, n_ in segs_py)} rows, query has {Lq}")
+    segs = (QSegment * len(segs_py))(*[QSegment(n_, o) for o, n_ in segs_py])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = lib.ra_ring_workspace_bytes(n, len(segs_py))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() < need or workspace.data_ptr() % 256 != 0:
+        raise RingAttentionError(f"workspace must hold {need} bytes at a 256-byte aligned address")
+    out = torch.empty((B, Hq, Lq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.ra_ring_attention(_dtype_code(q), B, Hq, Hkv, d, q.data_ptr(), segs, len(segs_py), descs, n,
+                               int(bool(causal)), float(scale), workspace.data_ptr(), workspace.numel(),
+                               out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q))
+    _check(lib, st, "ring_attention")
+    return (out, lse) if return_lse else out

@@ -1,0 +1,122 @@
+"""The C-ABI library loads and exports what its header declares (CPU only).
+
+No compute call is made here: only entry points whose host-side validation
+rejects the arguments before any HIP call, and pure-host helpers.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ring_attention_chunk_amd as ra
+from ring_attention_chunk_amd import api
+from ring_attention_chunk_amd.build import LIB, build_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ring_attention_chunk.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        build_library()
+    return ra.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared()
+    for n in ("ra_attention_chunk_stats", "ra_merge_chunk_stats", "ra_ring_attention"):
+        assert n in names
+    assert sorted(api.EXPORTS) == names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(ra_\w+)", out))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert lib.ra_status_string(0) == b"ok"
+    assert lib.ra_status_string(6) == b"workspace too small"
+    assert lib.ra_status_string(99) == b"unknown status"
+
+
+def test_workspace_size(lib):
+    assert lib.ra_ring_workspace_bytes(0, 1) % 256 == 0
+    assert lib.ra_ring_workspace_bytes(64, 2) >= 64 * 64 + 2 * 24
+    assert lib.ra_ring_workspace_bytes(100, 1) > lib.ra_ring_workspace_bytes(10, 1)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _ring(lib, dtype=1, B=1, Hq=2, Hkv=2, d=64, segs=None, nseg=1, chunks=None, nch=1, causal=0,
+          scale=0.125, ws=None, wsb=0, out=FAKE):
+    seg = (api.QSegment * 1)(api.QSegment(4, 0)) if segs is None else segs
+    ch = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 8, 0, 2 * 8 * 64, 8 * 64, 64)) if chunks is None else chunks
+    return lib.ra_ring_attention(dtype, B, Hq, Hkv, d, FAKE, seg, nseg, ch, nch, causal, scale, ws, wsb, out,
+                                 None, None)
+
+
+def test_ring_validation_codes(lib):
+    assert _ring(lib, dtype=7) == 3
+    assert _ring(lib, Hq=3, Hkv=2) == 2
+    assert _ring(lib, d=129) == 4
+    assert _ring(lib, d=0) == 4
+    assert _ring(lib, nseg=0) == 1
+    assert _ring(lib, scale=0.0) == 2
+    assert _ring(lib, scale=float("nan")) == 2
+    bad = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, -1, 0, 0, 0, 64))
+    assert _ring(lib, chunks=bad) == 2
+    bad = (api.KVChunk * 1)(api.KVChunk(None, FAKE, 8, 0, 0, 0, 64))
+    assert _ring(lib, chunks=bad) == 1
+    bad = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 8, -3, 0, 0, 64))
+    assert _ring(lib, chunks=bad) == 2
+    bad = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 8, 0, 0, 0, 32))  # row stride below head_dim
+    assert _ring(lib, chunks=bad) == 2
+    seg = (api.QSegment * 1)(api.QSegment(4, -1))
+    assert _ring(lib, segs=seg, causal=1) == 2
+    assert _ring(lib, out=None) == 1
+    assert _ring(lib, ws=None, wsb=0) == 6
+    assert _ring(lib, ws=ctypes.c_void_p(0x1010), wsb=1 << 20) == 6  # misaligned
+    assert b"workspace" in lib.ra_last_error()
+
+
+def test_empty_work_is_a_no_op(lib):
+    seg = (api.QSegment * 1)(api.QSegment(0, 0))
+    assert _ring(lib, segs=seg) == 0  # no queries: nothing to launch
+    assert _ring(lib, B=0) == 0
+    assert lib.ra_merge_chunk_stats(0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 0
+    assert lib.ra_last_error() == b""
+
+
+def test_stats_and_merge_validation(lib):
+    ch = api.KVChunk(FAKE, FAKE, 8, 0, 0, 0, 64)
+    assert lib.ra_attention_chunk_stats(1, 1, 2, 2, 64, FAKE, 4, None, 0.1, FAKE, FAKE, FAKE, None) == 1
+    assert lib.ra_attention_chunk_stats(1, 1, 2, 2, 64, FAKE, -1, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, None) == 2
+    assert lib.ra_attention_chunk_stats(1, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, None, FAKE, FAKE, None) == 1
+    assert lib.ra_attention_chunk_stats(2, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, None) == 3
+    assert lib.ra_merge_chunk_stats(-1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert lib.ra_merge_chunk_stats(5, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert lib.ra_merge_chunk_stats(5, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_python_layer_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ra.RingAttentionError):
+        ra.ring_attention(q, [q], [q])
+    with pytest.raises(ra.RingAttentionError):
+        ra.attention_chunk_stats(q, q, q)

@@ -1,0 +1,326 @@
+"""Parity of the HIP path with the fp64 oracle (needs an MI355X).
+
+Every call goes through the C ABI via the ctypes binding. Tolerances: fp32
+inputs max abs error <= 1e-5; bf16 inputs (fp32 accumulation) max abs error
+<= 2e-2 and mean abs error <= 2e-3, both against the oracle on the exact
+(upcast) inputs. The full-size shares are checked on sampled rows, each of
+which the oracle computes against every key.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_chunk_amd as ra
+from ring_attention_chunk_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+F32_TOL = 1e-5
+BF16_MAX, BF16_MEAN = 2e-2, 2e-3
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+def _check(got, ref, dtype):
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got))
+    if dtype == "f32":
+        assert err.max() <= F32_TOL, err.max()
+    else:
+        assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, (err.max(), err.mean())
+    return err.max()
+
+
+def _run(w, **kw):
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    offs = [o for o, _ in w.chunks]
+    out, lse = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, return_lse=True,
+                                 scale=w.softmax_scale, **kw)
+    torch.cuda.synchronize()
+    return q, kc, vc, offs, out, lse
+
+
+def _oracle(w, q, kc, vc, offs):
+    return oracle.attention(q.cpu(), [c.cpu() for c in kc], [c.cpu() for c in vc], wl.q_positions(w), offs,
+                            causal=w.causal, scale=w.softmax_scale)
+
+
+# ---------------------------------------------------------------------------
+# the pages' scalar example and the tiny fp32 share
+
+
+@pytest.mark.parametrize("order", [(0, 1), (1, 0)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scalar_two_shards(order, causal):
+    _say(f"scalar order={order} causal={causal}")
+    s = wl.scalar_case()
+    q = torch.from_numpy(s["q"]).to(DEV)
+    kc = [torch.from_numpy(s["k"][i]).to(DEV) for i in order]
+    vc = [torch.from_numpy(s["v"][i]).to(DEV) for i in order]
+    offs = [s["kv_offsets"][i] for i in order]
+    out = ra.ring_attention(q, kc, vc, 1, offs, causal=causal, scale=1.0)
+    torch.cuda.synchronize()
+    exact = math.exp(10) / (1 + math.exp(10))
+    assert abs(out.item() - exact) <= F32_TOL
+    assert abs(out.item() - 0.5) > 0.4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_f32_every_listed_split_is_bit_identical(causal):
+    w = wl.tiny(causal)
+    _say(w.name)
+    q, kc, vc, offs, out, lse = _run(w)
+    ref = _oracle(w, q, kc, vc, offs)
+    _check(_np(out), ref["out"], "f32")
+    assert np.abs(_np(lse) - ref["lse"]).max() <= F32_TOL
+    rng = np.random.default_rng(1)
+    splits = [list(range(1, 32)), [], [16], [5, 6, 7, 30]]
+    splits += [sorted(rng.choice(np.arange(1, 32), size=int(rng.integers(1, 10)), replace=False)) for _ in range(20)]
+    for cuts in splits:
+        r = wl.resplit(w, cuts)
+        _, _, _, _, out2, lse2 = _run(r)
+        assert torch.equal(out2, out), cuts
+        assert torch.equal(lse2, lse), cuts
+
+
+def test_tiny_chunk_stats_and_merge_f32():
+    w = wl.tiny(False)
+    _say("tiny stats+merge")
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    acc = None
+    ref_acc = None
+    for c in range(len(kc)):
+        st = ra.attention_chunk_stats(q, kc[c], vc[c])
+        torch.cuda.synchronize()
+        r = oracle.chunk_stats(q.cpu(), kc[c].cpu(), vc[c].cpu(), 1 / math.sqrt(16))
+        # statistics compared in normalised form and as log-sum-exp
+        assert np.abs(_np(st[2]) - r[2]).max() <= F32_TOL
+        assert np.abs(_np(st[0]) / _np(st[1])[..., None] - r[0] / r[1][..., None]).max() <= F32_TOL
+        assert np.abs(np.log(_np(st[1])) + _np(st[2]) - (np.log(r[1]) + r[2])).max() <= F32_TOL
+        acc = st if acc is None else ra.merge_chunk_stats(acc, st)
+        ref_acc = r if ref_acc is None else oracle.merge_chunk_stats(ref_acc, r)
+    torch.cuda.synchronize()
+    out = _np(acc[0]) / _np(acc[1])[..., None]
+    direct = oracle.attention(q.cpu(), [k.cpu()], [v.cpu()])
+    _check(out, direct["out"], "f32")
+    assert np.abs(_np(acc[2]) - ref_acc[2]).max() <= F32_TOL
+
+
+# ---------------------------------------------------------------------------
+# small bf16 / fp32 shares that span several tiles, with ragged tails
+
+
+SMALL = [
+    # name, dtype, B, Hq, Hkv, d, q_segments, chunks, causal
+    ("bf16_d64_nc", "bf16", 2, 4, 2, 64, [(0, 300)], [(0, 100), (100, 37), (137, 250), (387, 1), (388, 130)], False),
+    ("bf16_d128_causal", "bf16", 1, 3, 3, 128, [(200, 260)], [(0, 64), (64, 200), (264, 236)], True),
+    ("bf16_d128_zigzag", "bf16", 1, 2, 1, 128, [(64, 64), (448, 64)],
+     [(64 * j, 64) for j in (1, 6, 0, 7, 3, 4, 2, 5)], True),
+    ("bf16_d40_causal_gqa", "bf16", 1, 4, 1, 40, [(90, 150)], [(0, 33), (33, 200)], True),
+    ("bf16_d8_nc", "bf16", 1, 1, 1, 8, [(0, 129)], [(0, 65), (65, 1)], False),
+    ("bf16_d100_nc", "bf16", 1, 2, 2, 100, [(0, 77)], [(0, 190)], False),
+    ("f32_d64_causal", "f32", 1, 2, 2, 64, [(100, 140)], [(0, 120), (120, 120)], True),
+    ("f32_d128_nc", "f32", 1, 2, 1, 128, [(0, 70)], [(0, 90), (90, 50)], False),
+    ("f32_d3_nc", "f32", 1, 2, 2, 3, [(0, 33)], [(0, 5), (5, 60)], False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shares(case):
+    name, dtype, B, Hq, Hkv, d, qs, ch, causal = case
+    _say(name)
+    w = wl.custom(name, dtype, B, Hq, Hkv, d, qs, ch, causal, seed=hash(name) % 1000)
+    q, kc, vc, offs, out, lse = _run(w)
+    ref = _oracle(w, q, kc, vc, offs)
+    _check(_np(out), ref["out"], dtype)
+    tol = F32_TOL if dtype == "f32" else 1e-2
+    assert np.abs(_np(lse) - ref["lse"]).max() <= tol
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("bf16", 24), ("f32", 32)])
+def test_chunk_stats_small(dtype, d):
+    _say(f"chunk_stats {dtype} d={d}")
+    w = wl.custom("st", dtype, 2, 4, 2, d, [(0, 200)], [(0, 333)], False, seed=d)
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    u, l, m = ra.attention_chunk_stats(q, kc[0], vc[0])
+    torch.cuda.synchronize()
+    ru, rl, rm = oracle.chunk_stats(q.cpu(), np.repeat(kc[0].cpu().float().numpy(), 2, axis=1),
+                                    np.repeat(vc[0].cpu().float().numpy(), 2, axis=1), 1 / math.sqrt(d))
+    _check(_np(u) / _np(l)[..., None], ru / rl[..., None], dtype)
+    assert np.abs(_np(m) - rm).max() <= (F32_TOL if dtype == "f32" else 1e-4) * max(1, np.abs(rm).max())
+    assert np.abs(np.log(_np(l)) + _np(m) - (np.log(rl) + rm)).max() <= (F32_TOL if dtype == "f32" else 1e-2)
+
+
+def test_merge_random_statistics():
+    _say("merge random")
+    g = torch.Generator().manual_seed(3)
+    for d in (128, 64, 5, 1):
+        rows = 1000
+        a = (torch.randn(rows, d, generator=g), torch.rand(rows, generator=g) + 0.5, torch.randn(rows, generator=g) * 8)
+        b = (torch.randn(rows, d, generator=g), torch.rand(rows, generator=g) + 0.5, torch.randn(rows, generator=g) * 8)
+        # rows with nothing seen yet on one or both sides
+        a[2][:10] = -math.inf
+        a[1][:10] = 0
+        a[0][:10] = 0
+        b[2][5:15] = -math.inf
+        b[1][5:15] = 0
+        b[0][5:15] = 0
+        ga = tuple(t.to(DEV) for t in a)
+        gb = tuple(t.to(DEV) for t in b)
+        u, l, m = ra.merge_chunk_stats(ga, gb)
+        torch.cuda.synchronize()
+        ru, rl, rm = oracle.merge_chunk_stats(tuple(t.double().numpy() for t in a), tuple(t.double().numpy() for t in b))
+        assert np.array_equal(np.isneginf(_np(m)), np.isneginf(rm))
+        fin = ~np.isneginf(rm)
+        assert np.abs(_np(m)[fin] - rm[fin]).max() == 0.0
+        assert np.abs(_np(l) - rl).max() <= 1e-5 * max(1.0, np.abs(rl).max())
+        assert np.abs(_np(u) - ru).max() <= 1e-5 * max(1.0, np.abs(ru).max())
+        # in place
+        ua, la, ma = (t.clone() for t in ga)
+        ra.merge_chunk_stats((ua, la, ma), gb, inplace=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ua, u) and torch.equal(la, l) and torch.equal(ma, m)
+
+
+def test_stats_merge_composition_matches_ring():
+    _say("stats+merge vs ring")
+    w = wl.custom("comp", "bf16", 1, 4, 4, 128, [(0, 256)], [(0, 300), (300, 200), (500, 12)], False, seed=5)
+    q, kc, vc, offs, out, lse = _run(w)
+    acc = None
+    for k, v in zip(kc, vc):
+        st = ra.attention_chunk_stats(q, k, v)
+        acc = st if acc is None else ra.merge_chunk_stats(acc, st)
+    torch.cuda.synchronize()
+    comp = acc[0] / acc[1][..., None]
+    ref = _oracle(w, q, kc, vc, offs)
+    _check(_np(comp), ref["out"], "bf16")
+    assert (comp - out).abs().max().item() <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+
+
+def test_edges():
+    _say("edges")
+    q = torch.randn(1, 2, 5, 64, device=DEV).to(torch.bfloat16)
+    e = torch.empty(1, 2, 0, 64, device=DEV, dtype=torch.bfloat16)
+    out, lse = ra.ring_attention(q, [e, e], [e, e], 0, [0, 0], causal=False, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    out, lse = ra.ring_attention(q, [], [], 0, [], causal=False, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    # queries before every key: nothing is visible
+    k = torch.randn(1, 2, 70, 64, device=DEV).to(torch.bfloat16)
+    out, lse = ra.ring_attention(q, [k], [k], 0, [100], causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    # a query whose only visible key is its own position returns that key's value
+    out = ra.ring_attention(q[:, :, :1], [k], [k * 3], 100, [100], causal=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(out[0, :, 0], (k * 3)[0, :, 0].float(), atol=0, rtol=0)
+    # no queries
+    z = ra.ring_attention(q[:, :, :0], [k], [k], 0, [0])
+    assert z.shape == (1, 2, 0, 64)
+    u, l, m = ra.attention_chunk_stats(q, e, e)
+    torch.cuda.synchronize()
+    assert torch.all(u == 0) and torch.all(l == 0) and torch.all(torch.isneginf(m))
+
+
+def test_errors_raise():
+    _say("errors")
+    q = torch.randn(1, 3, 5, 64, device=DEV).to(torch.bfloat16)
+    k = torch.randn(1, 2, 7, 64, device=DEV).to(torch.bfloat16)
+    with pytest.raises(ra.RingAttentionError):
+        ra.ring_attention(q, [k], [k])  # 3 query heads on 2 kv heads
+    with pytest.raises(ra.RingAttentionError):
+        ra.ring_attention(q, [k], [k.float()])
+    big = torch.randn(1, 1, 4, 130, device=DEV).to(torch.bfloat16)
+    with pytest.raises(ra.RingAttentionError):
+        ra.ring_attention(big, [big], [big])
+    with pytest.raises(ra.RingAttentionError):
+        ra.ring_attention(q[:, :2], [k], [k], 0, [-5], causal=True)
+
+
+# ---------------------------------------------------------------------------
+# determinism and causal isolation on the GPU
+
+
+def test_causal_future_perturbation_is_bitwise_invisible():
+    _say("causal perturbation")
+    w = wl.custom("pert", "bf16", 1, 2, 2, 128, [(300, 200)], [(0, 256), (256, 256), (512, 256)], True, seed=9)
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    offs = [o for o, _ in w.chunks]
+    out = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=True)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 420:] = torch.randn_like(k2[:, :, 420:].float()).to(torch.bfloat16) * 5
+    v2[:, :, 420:] = 7
+    kc2 = [k2[:, :, o:o + n] for o, n in w.chunks]
+    vc2 = [v2[:, :, o:o + n] for o, n in w.chunks]
+    out2 = ra.ring_attention(q, kc2, vc2, w.q_segments, offs, causal=True)
+    torch.cuda.synchronize()
+    # rows at positions < 420 see none of the changed keys
+    assert torch.equal(out[:, :, :120], out2[:, :, :120])
+    assert not torch.equal(out[:, :, 121:], out2[:, :, 121:])
+
+
+# ---------------------------------------------------------------------------
+# the four full-size shares, in the launch configuration the benchmark times
+
+_CACHE = {}
+
+
+def _full(i):
+    if i not in _CACHE:
+        _CACHE.clear()
+        w = wl.config(i)
+        _CACHE[i] = (w, wl.generate_torch(w, DEV))
+    return _CACHE[i]
+
+
+@pytest.mark.parametrize("i,nrows", [(1, 512), (2, 384), (3, 384), (4, 128)])
+def test_full_size_sampled_rows(i, nrows):
+    w, (q, k, v, kc, vc) = _full(i)
+    _say(f"{w.name} sampled {nrows}")
+    offs = [o for o, _ in w.chunks]
+    out, lse = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    rows = wl.sample_rows(w, nrows, seed=i)
+    ref = oracle.attention_rows(q.cpu(), [c.cpu() for c in kc], [c.cpu() for c in vc], rows,
+                                wl.q_positions(w), offs, causal=w.causal)
+    idx = tuple(np.array(rows).T)
+    got = out.cpu().double().numpy()[idx]
+    _check(got, ref["out"], "bf16")
+    assert np.abs(lse.cpu().double().numpy()[idx] - ref["lse"]).max() <= 1e-2
+    # repeat run: bit-identical
+    out2 = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("i", [1, 3])
+def test_full_size_resplit_is_bit_identical(i):
+    w, (q, k, v, kc, vc) = _full(i)
+    _say(f"{w.name} resplit")
+    offs = [o for o, _ in w.chunks]
+    out = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal)
+    cuts = [1000, 4096 + 3096, 5 * 4096 + 77, w.lk // 2 + 1]
+    r = wl.resplit(w, cuts)
+    kc2 = [k[:, :, o:o + n] for o, n in r.chunks]
+    vc2 = [v[:, :, o:o + n] for o, n in r.chunks]
+    out2 = ra.ring_attention(q, kc2, vc2, w.q_segments, [o for o, _ in r.chunks], causal=w.causal)
+    torch.cuda.synchronize()
+    assert len(r.chunks) > len(w.chunks)
+    assert torch.equal(out, out2)
