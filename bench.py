@@ -133,7 +133,7 @@ def main():
     q, k, v, kc, vc = wl.generate_torch(w, dev)
     offs = [o for o, _ in w.chunks]
     flops = wl.counted_flops(w)
-    ws = torch.empty(ra.api.load_library().ra_ring_workspace_bytes(len(kc), len(w.q_segments)),
+    ws = torch.empty(ra.api.workspace_bytes(tuple(q.shape), [c.shape[2] for c in kc], len(w.q_segments)),
                      dtype=torch.uint8, device=dev)
 
     def step():

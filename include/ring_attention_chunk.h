@@ -105,9 +105,12 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
 int ra_merge_chunk_stats(int64_t rows, int head_dim, float* acc_u, float* acc_l, float* acc_m,
                          const float* u, const float* l, const float* m, void* stream);
 
-/* Device workspace, in bytes, that ra_ring_attention needs for n_chunks chunk
- * descriptors and n_q_segments query segments (a multiple of 256). */
-size_t ra_ring_workspace_bytes(int n_chunks, int n_q_segments);
+/* Device workspace, in bytes, that ra_ring_attention needs for this shape:
+ * the chunk descriptor and query segment tables and, when the query tiles
+ * alone cannot fill the GPU, room for per-key-range partial statistics
+ * (fp32, (head_dim + 2) values per row and range). A multiple of 256. */
+size_t ra_ring_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys,
+                               int n_chunks, int n_q_segments);
 
 /* ring_attention(query, key_chunks, value_chunks, q_global_offset,
  * kv_global_offsets, causal) -> normalised output.
@@ -121,10 +124,13 @@ size_t ra_ring_workspace_bytes(int n_chunks, int n_q_segments);
  *  q_segments  host array of n_q_segments runs whose lengths sum to q_len
  *              (n_q_segments >= 1); positions matter only when causal.
  *  chunks      host array of n_chunks descriptors in ring order (n_chunks >= 0).
- *  workspace   device buffer of >= ra_ring_workspace_bytes(n_chunks,
- *              n_q_segments) bytes, 256-byte aligned; the descriptor table is
- *              copied there on `stream` (stream-ordered), so two calls on one
- *              stream may share it, calls on different streams may not.
+ *  workspace   device buffer of >= ra_ring_workspace_bytes(batch, q_heads,
+ *              head_dim, q_len, total_keys, n_chunks, n_q_segments) bytes,
+ *              256-byte aligned, where total_keys is the sum of the chunk
+ *              lengths; the descriptor tables are copied there on `stream`
+ *              (stream-ordered) and partial statistics may be written there,
+ *              so two calls on one stream may share it, calls on different
+ *              streams may not.
  *  out         [B,Hq,q_len,d] fp32; lse [B,Hq,q_len] fp32 or NULL.
  * For a fixed ordered key sequence the output is bit-identical for every split
  * of that sequence into chunks and from run to run. */

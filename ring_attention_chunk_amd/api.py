@@ -71,7 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_attention_chunk_stats.restype = i32
     lib.ra_merge_chunk_stats.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.ra_merge_chunk_stats.restype = i32
-    lib.ra_ring_workspace_bytes.argtypes = [i32, i32]
+    lib.ra_ring_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32, i32]
     lib.ra_ring_workspace_bytes.restype = sz
     lib.ra_ring_attention.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                       ctypes.POINTER(KVChunk), i32, i32, f32, vp, sz, vp, vp, vp]
@@ -196,6 +196,13 @@ def merge_chunk_stats(acc, chunk, inplace: bool = False):
 QOffset = Union[int, Sequence[Tuple[int, int]]]
 
 
+def workspace_bytes(query_shape, key_lengths, n_q_segments: int = 1) -> int:
+    """Bytes of device workspace ``ring_attention`` needs for this shape."""
+    B, Hq, Lq, d = query_shape
+    return int(load_library().ra_ring_workspace_bytes(B, Hq, d, Lq, int(sum(key_lengths)), len(key_lengths),
+                                                      n_q_segments))
+
+
 def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global_offset: QOffset = 0,
                    kv_global_offsets: Optional[Sequence[int]] = None, causal: bool = False,
                    scale: Optional[float] = None, return_lse: bool = False, workspace=None):
@@ -240,7 +247,8 @@ def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global
     segs = (QSegment * len(segs_py))(*[QSegment(n_, o) for o, n_ in segs_py])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = lib.ra_ring_workspace_bytes(n, len(segs_py))
+    total_keys = sum(int(k.shape[2]) for k in key_chunks)
+    need = lib.ra_ring_workspace_bytes(B, Hq, d, Lq, total_keys, n, len(segs_py))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace.numel() < need or workspace.data_ptr() % 256 != 0:

@@ -20,13 +20,19 @@
 //    plus one exchange with lane l ^ 32. The probabilities stay in registers
 //    and feed O^T = V^T P^T directly as the B operand (the key order inside a
 //    16-key slice is permuted; V^T is stored in LDS with the same permutation).
-//  * K tiles are staged row-major in LDS, V tiles transposed (d-major); both
-//    are double-buffered, and the next tile is fetched from HBM into registers
-//    while the current one is computed.
+//  * K and V tiles are double-buffered in LDS; the next tile is fetched from
+//    HBM into registers while the current one is computed, so each tile costs
+//    one workgroup barrier. The fetch of a tile that lies in one chunk is
+//    straight-line vector loads; the loads go through global-address-space
+//    pointers so that waiting on LDS never waits on the HBM prefetch.
 //  * With a causal mask, each tile is classified from global positions: tiles
 //    whose first key lies after every query of the workgroup are skipped (and
 //    whole chunks at once), tiles entirely in the past need no mask, the rest
 //    compare positions per element (positions, never local indices).
+//  * When (batch x heads x query tiles) is too small to fill the chip, the key
+//    tiles are cut into equal ranges handled by separate workgroups; their
+//    partial (u, l, m) are merged in range order by a second kernel. The cut
+//    depends only on the number of keys, never on the chunk list.
 //  * fp32 inputs take the same path with v_mfma_f32_32x32x2f32.
 //  * The merge of two statistics is a separate bandwidth-bound kernel.
 
@@ -34,9 +40,9 @@
 
 #include <math.h>
 #include <stdarg.h>
-#include <stdlib.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "ring_attention_chunk.h"
@@ -53,9 +59,10 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;  // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
-constexpr int kPosNone = 0x7fffffff;          // position of a missing key: after everything
-constexpr int kPosAll = 0x7ffffffe;           // query position that allows every real key
-constexpr int kPosMin = -0x7fffffff - 1;      // query position of a missing row
+constexpr int kPosNone = 0x7fffffff;      // position of a missing key: after everything
+constexpr int kPosAll = 0x7ffffffe;       // query position that allows every real key
+constexpr int kPosMin = -0x7fffffff - 1;  // query position of a missing row
+constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode { kStats = 0, kRingFull = 1, kRingCausal = 2 };
 
@@ -81,6 +88,7 @@ struct Params {
   float* o;    // out (ring) or u (stats)
   float* l;    // lse (ring, may be null) or l (stats)
   float* m;    // m (stats)
+  float* part; // split partials: u [nsplit][rows][d], then l and m [nsplit][rows]
   const ChunkDev* chunks;
   const QSegDev* qsegs;
   ChunkDev one;  // the single chunk of the stats call
@@ -88,12 +96,23 @@ struct Params {
   int n_chunks, n_qseg;
   int B, Hq, Hkv, d;
   int n_qt;
+  int nsplit;   // key-tile ranges per (batch, head, query tile)
   int vec;      // 16-byte loads allowed for q, k and v
   float scale;  // softmax scale
   float c2;     // scale * log2(e)
 };
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
+
+// Loads through global-address-space pointers. Pointers read from the chunk
+// table carry no address space; generic (flat) loads would also count against
+// the LDS wait counter and make every LDS wait drain the HBM prefetch.
+typedef const u32x4 __attribute__((address_space(1)))* gptr_u32x4;
+typedef const uint16_t __attribute__((address_space(1)))* gptr_u16;
+typedef const float __attribute__((address_space(1)))* gptr_f32;
+__device__ __forceinline__ u32x4 gload16(const void* ptr) { return *(gptr_u32x4)ptr; }
+__device__ __forceinline__ uint32_t gload_u16(const void* ptr) { return *(gptr_u16)ptr; }
+__device__ __forceinline__ float gload_f32(const void* ptr) { return *(gptr_f32)ptr; }
 
 template <int MODE>
 __device__ __forceinline__ ChunkDev chunk_at(const Params& p, int c) {
@@ -105,338 +124,26 @@ __device__ __forceinline__ ChunkDev chunk_at(const Params& p, int c) {
 }
 
 // ---------------------------------------------------------------------------
-// Element-type specific pieces: LDS layout, tile staging, MFMA fragments.
-
-template <class T, int DP>
-struct Ops;
-
-// bf16: K row-major [BN][DP + 8], V transposed [DP][BN + 8] with the key order of
-// each 16-key slice permuted (quads 1 and 2 swapped) to match the P fragments.
-template <int DP>
-struct Ops<__bf16, DP> {
-  static constexpr int KP = DP + 8;
-  static constexpr int VP = BN + 8;
-  static constexpr int K_BYTES = BN * KP * 2;
-  static constexpr int V_BYTES = DP * VP * 2;
-  static constexpr int BUF_BYTES = K_BYTES + V_BYTES + BN * 4;
-  static constexpr int CPR = DP / 8;                                   // 16-byte chunks per row
-  static constexpr int NK = (BN * CPR + kThreads - 1) / kThreads;      // K items per thread
-  static constexpr int NV = ((BN / 4) * CPR + kThreads - 1) / kThreads;  // V quad items per thread
-  static constexpr int QF = DP / 16;
-
-  struct Stage {
-    u32x4 k[NK];
-    u32x4 v[NV][4];
-    int pos[NK];
-  };
-  struct QFrag {
-    bf16x8 f[QF];
-  };
-
-  static __device__ __forceinline__ u32x4 load16(const __bf16* row, int c0, int d, bool vec) {
-    if (vec) {
-      if (c0 < d) return *(const u32x4*)(row + c0);
-      return u32x4{0, 0, 0, 0};
-    }
-    const uint16_t* r = (const uint16_t*)row;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = (c0 + 2 * i < d) ? r[c0 + 2 * i] : 0u;
-      uint32_t hi = (c0 + 2 * i + 1 < d) ? r[c0 + 2 * i + 1] : 0u;
-      w[i] = lo | (hi << 16);
-    }
-    return u32x4{w[0], w[1], w[2], w[3]};
-  }
-
-  static __device__ __forceinline__ void load_q(const Params& p, const __bf16* qrow, bool valid,
-                                                int h, QFrag& q) {
-#pragma unroll
-    for (int kk = 0; kk < QF; ++kk) {
-      u32x4 x = valid ? load16(qrow, kk * 16 + h * 8, p.d, p.vec) : u32x4{0, 0, 0, 0};
-      q.f[kk] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  // Scores of one 32-key block of the tile (raw dot products), transposed.
-  static __device__ __forceinline__ f32x16 qk(const char* buf, const QFrag& q, int kb, int lane) {
-    const __bf16* Ks = (const __bf16*)buf;
-    const __bf16* base = Ks + (kb * 32 + (lane & 31)) * KP + (lane >> 5) * 8;
-    f32x16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < QF; ++kk) {
-      bf16x8 a = *(const bf16x8*)(base + kk * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.f[kk], acc, 0, 0, 0);
-    }
-    return acc;
-  }
-
-  // o[db] += V^T P^T over the tile, P taken from the (exponentiated) score blocks.
-  static __device__ __forceinline__ void pv(const char* buf, const f32x16* s, f32x16* o, int lane) {
-    const __bf16* Vs = (const __bf16*)(buf + K_BYTES);
-    bf16x8 pf[BN / 16];
-#pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) pf[ks][t] = (__bf16)s[ks >> 1][(ks & 1) * 8 + t];
-    }
-#pragma unroll
-    for (int db = 0; db < DP / 32; ++db) {
-      const __bf16* vrow = Vs + (db * 32 + (lane & 31)) * VP + (lane >> 5) * 8;
-#pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) {
-        bf16x8 a = *(const bf16x8*)(vrow + ks * 16);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
-      }
-    }
-  }
-
-  static __device__ __forceinline__ uint32_t pick(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi_src, lo_src, sel);
-  }
-
-  static __device__ __forceinline__ void store(char* buf, const Stage& st, int tid) {
-    __bf16* Ks = (__bf16*)buf;
-    __bf16* Vs = (__bf16*)(buf + K_BYTES);
-    int* P = (int*)(buf + K_BYTES + V_BYTES);
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      int item = tid + i * kThreads;
-      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
-        int r = item / CPR, cc = item % CPR;
-        *(u32x4*)(Ks + r * KP + cc * 8) = st.k[i];
-        if (cc == 0) P[r] = st.pos[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int item = tid + i * kThreads;
-      if (((BN / 4) * CPR) % kThreads == 0 || item < (BN / 4) * CPR) {
-        int qd = item % (BN / 4), cc = item / (BN / 4);
-        int qi = qd & 3;
-        int pq = (qd & ~3) | (qi == 1 ? 2 : (qi == 2 ? 1 : qi));
-        const u32x4* r = st.v[i];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // dword w of each key row holds d = 2w (low half) and d = 2w + 1 (high half)
-          uint32_t e0 = pick(r[1][w], r[0][w], 0x05040100u);
-          uint32_t e1 = pick(r[3][w], r[2][w], 0x05040100u);
-          uint32_t o0 = pick(r[1][w], r[0][w], 0x07060302u);
-          uint32_t o1 = pick(r[3][w], r[2][w], 0x07060302u);
-          *(u32x2*)(Vs + (cc * 8 + 2 * w) * VP + pq * 4) = u32x2{e0, e1};
-          *(u32x2*)(Vs + (cc * 8 + 2 * w + 1) * VP + pq * 4) = u32x2{o0, o1};
-        }
-      }
-    }
-  }
-
-  // Fetch tile rows [t0, t0 + BN) from HBM into registers.
-  template <int MODE>
-  static __device__ __forceinline__ void fetch(const Params& p, int64_t t0, int cursor, bool one_chunk,
-                                               int b, int hk, int tid, Stage& st) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      int item = tid + i * kThreads;
-      st.k[i] = u32x4{0, 0, 0, 0};
-      st.pos[i] = kPosNone;
-      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
-        int r = item / CPR, cc = item % CPR;
-        const __bf16* kr;
-        const __bf16* vr;
-        int pos;
-        if (row_src<MODE>(p, t0 + r, cursor, one_chunk, b, hk, kr, vr, pos)) {
-          st.k[i] = load16(kr, cc * 8, p.d, p.vec);
-          st.pos[i] = pos;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int item = tid + i * kThreads;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) st.v[i][w] = u32x4{0, 0, 0, 0};
-      if (((BN / 4) * CPR) % kThreads == 0 || item < (BN / 4) * CPR) {
-        int qd = item % (BN / 4), cc = item / (BN / 4);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const __bf16* kr;
-          const __bf16* vr;
-          int pos;
-          if (row_src<MODE>(p, t0 + qd * 4 + w, cursor, one_chunk, b, hk, kr, vr, pos))
-            st.v[i][w] = load16(vr, cc * 8, p.d, p.vec);
-        }
-      }
-    }
-  }
-
-  // Source rows of concatenated key index j (false if j is past the last key).
-  template <int MODE>
-  static __device__ __forceinline__ bool row_src(const Params& p, int64_t j, int cursor, bool one_chunk,
-                                                 int b, int hk, const __bf16*& kr, const __bf16*& vr,
-                                                 int& pos) {
-    if (j >= p.Lk) return false;
-    int c = cursor;
-    if (!one_chunk) {
-      while (c + 1 < p.n_chunks) {
-        ChunkDev ch = chunk_at<MODE>(p, c);
-        if (j < ch.start + ch.len) break;
-        ++c;
-      }
-    }
-    ChunkDev ch = chunk_at<MODE>(p, c);
-    int64_t off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j - ch.start) * ch.ss;
-    kr = (const __bf16*)ch.k + off;
-    vr = (const __bf16*)ch.v + off;
-    pos = ch.pos0 + (int)(j - ch.start);
-    return true;
-  }
-};
-
-// fp32: K and V both row-major [BN][DP + 4]; fragments for v_mfma_f32_32x32x2f32.
-template <int DP>
-struct Ops<float, DP> {
-  static constexpr int KP = DP + 4;
-  static constexpr int K_BYTES = BN * KP * 4;
-  static constexpr int V_BYTES = BN * KP * 4;
-  static constexpr int BUF_BYTES = K_BYTES + V_BYTES + BN * 4;
-  static constexpr int CPR = DP / 4;
-  static constexpr int NK = (BN * CPR + kThreads - 1) / kThreads;
-  static constexpr int QF = DP / 2;
-
-  struct Stage {
-    u32x4 k[NK];
-    u32x4 v[NK];
-    int pos[NK];
-  };
-  struct QFrag {
-    float f[QF];
-  };
-
-  static __device__ __forceinline__ u32x4 load16(const float* row, int c0, int d, bool vec) {
-    if (vec) {
-      if (c0 < d) return *(const u32x4*)(row + c0);
-      return u32x4{0, 0, 0, 0};
-    }
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (c0 + i < d) ? __float_as_uint(row[c0 + i]) : 0u;
-    return u32x4{w[0], w[1], w[2], w[3]};
-  }
-
-  static __device__ __forceinline__ void load_q(const Params& p, const float* qrow, bool valid, int h,
-                                                QFrag& q) {
-#pragma unroll
-    for (int kk = 0; kk < QF; ++kk) {
-      int c = 2 * kk + h;
-      q.f[kk] = (valid && c < p.d) ? qrow[c] : 0.f;
-    }
-  }
-
-  static __device__ __forceinline__ f32x16 qk(const char* buf, const QFrag& q, int kb, int lane) {
-    const float* Ks = (const float*)buf;
-    const float* base = Ks + (kb * 32 + (lane & 31)) * KP + (lane >> 5);
-    f32x16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < QF; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(base[2 * kk], q.f[kk], acc, 0, 0, 0);
-    return acc;
-  }
-
-  static __device__ __forceinline__ void pv(const char* buf, const f32x16* s, f32x16* o, int lane) {
-    const float* Vs = (const float*)(buf + K_BYTES);
-    const int h = lane >> 5;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-#pragma unroll
-        for (int db = 0; db < DP / 32; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * KP + db * 32 + (lane & 31)], s[kb][r],
-                                                       o[db], 0, 0, 0);
-      }
-    }
-  }
-
-  static __device__ __forceinline__ void store(char* buf, const Stage& st, int tid) {
-    float* Ks = (float*)buf;
-    float* Vs = (float*)(buf + K_BYTES);
-    int* P = (int*)(buf + K_BYTES + V_BYTES);
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      int item = tid + i * kThreads;
-      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
-        int r = item / CPR, cc = item % CPR;
-        *(u32x4*)(Ks + r * KP + cc * 4) = st.k[i];
-        *(u32x4*)(Vs + r * KP + cc * 4) = st.v[i];
-        if (cc == 0) P[r] = st.pos[i];
-      }
-    }
-  }
-
-  template <int MODE>
-  static __device__ __forceinline__ void fetch(const Params& p, int64_t t0, int cursor, bool one_chunk,
-                                               int b, int hk, int tid, Stage& st) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      int item = tid + i * kThreads;
-      st.k[i] = u32x4{0, 0, 0, 0};
-      st.v[i] = u32x4{0, 0, 0, 0};
-      st.pos[i] = kPosNone;
-      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
-        int r = item / CPR, cc = item % CPR;
-        const float* kr;
-        const float* vr;
-        int pos;
-        if (row_src<MODE>(p, t0 + r, cursor, one_chunk, b, hk, kr, vr, pos)) {
-          st.k[i] = load16(kr, cc * 4, p.d, p.vec);
-          st.v[i] = load16(vr, cc * 4, p.d, p.vec);
-          st.pos[i] = pos;
-        }
-      }
-    }
-  }
-
-  template <int MODE>
-  static __device__ __forceinline__ bool row_src(const Params& p, int64_t j, int cursor, bool one_chunk,
-                                                 int b, int hk, const float*& kr, const float*& vr,
-                                                 int& pos) {
-    if (j >= p.Lk) return false;
-    int c = cursor;
-    if (!one_chunk) {
-      while (c + 1 < p.n_chunks) {
-        ChunkDev ch = chunk_at<MODE>(p, c);
-        if (j < ch.start + ch.len) break;
-        ++c;
-      }
-    }
-    ChunkDev ch = chunk_at<MODE>(p, c);
-    int64_t off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j - ch.start) * ch.ss;
-    kr = (const float*)ch.k + off;
-    vr = (const float*)ch.v + off;
-    pos = ch.pos0 + (int)(j - ch.start);
-    return true;
-  }
-};
-
-// ---------------------------------------------------------------------------
 // Tile walk (uniform across the workgroup): find the next tile at or after t
 // that holds at least one key some query of the workgroup may see.
 
 struct TileInfo {
-  int64_t t;      // tile index (== ntiles when the walk is over)
-  int cursor;     // chunk containing the tile's first key
-  bool one_chunk; // all keys of the tile come from chunk `cursor`
-  bool tail;      // the tile runs past the last key
-  int kmin, kmax; // smallest / largest global key position in the tile
+  int t;           // tile index (== end when the walk is over)
+  int cursor;      // chunk containing the tile's first key
+  int flags;       // bit 0: all keys from chunk `cursor`; bit 1: the tile runs past the last key
+  int kmin, kmax;  // smallest / largest global key position in the tile (causal only)
+  int pos0;        // global position of the tile's first row if it lies in one chunk
+  int ss;          // element stride between rows of chunk `cursor`
+  const char* kp;  // address of the tile's first key row (batch and head applied)
+  const char* vp;  // same for values
 };
 
-template <int MODE>
-__device__ __forceinline__ TileInfo next_tile(const Params& p, int64_t t, int cursor, int64_t ntiles,
-                                              int qmax) {
+template <int MODE, int ELEM>
+__device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor, int end, int qmax, int b,
+                                              int hk) {
   TileInfo ti;
-  while (t < ntiles) {
-    const int64_t t0 = t * BN;
+  while (t < end) {
+    const int64_t t0 = (int64_t)t * BN;
     const int64_t t1 = min(t0 + (int64_t)BN, p.Lk);
     // advance the cursor to the chunk holding key t0 (zero-length chunks are passed over)
     ChunkDev ch = chunk_at<MODE>(p, cursor);
@@ -445,12 +152,12 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int64_t t, int cu
       ch = chunk_at<MODE>(p, cursor);
     }
     int kmin = kPosNone, kmax = kPosMin;
-    bool one = (t1 <= ch.start + ch.len);
+    const bool one = (t1 <= ch.start + ch.len);
     if (MODE == kRingCausal) {
       int c = cursor;
       ChunkDev cc = ch;
       while (true) {
-        int64_t lo = max(t0, cc.start), hi = min(t1, cc.start + cc.len);
+        const int64_t lo = max(t0, cc.start), hi = min(t1, cc.start + cc.len);
         if (lo < hi) {
           kmin = min(kmin, cc.pos0 + (int)(lo - cc.start));
           kmax = max(kmax, cc.pos0 + (int)(hi - 1 - cc.start));
@@ -462,7 +169,7 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int64_t t, int cu
       if (kmin > qmax) {
         // nothing here is visible; if the whole chunk is in the future, jump past it
         if (one && ch.pos0 > qmax) {
-          int64_t nt = (ch.start + ch.len) / BN;
+          const int nt = (int)((ch.start + ch.len) / BN);
           t = nt > t ? nt : t + 1;
         } else {
           ++t;
@@ -470,22 +177,398 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int64_t t, int cu
         continue;
       }
     }
+    const int64_t off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (t0 - ch.start) * ch.ss;
     ti.t = t;
     ti.cursor = cursor;
-    ti.one_chunk = one;
-    ti.tail = (t0 + BN > p.Lk);
+    ti.flags = (one ? 1 : 0) | ((t0 + BN > p.Lk) ? 2 : 0);
     ti.kmin = kmin;
     ti.kmax = kmax;
+    ti.pos0 = ch.pos0 + (int)(t0 - ch.start);
+    ti.ss = (int)ch.ss;
+    ti.kp = (const char*)ch.k + off * ELEM;
+    ti.vp = (const char*)ch.v + off * ELEM;
     return ti;
   }
-  ti.t = ntiles;
+  ti.t = end;
   ti.cursor = cursor;
-  ti.one_chunk = true;
-  ti.tail = false;
+  ti.flags = 1;
   ti.kmin = kPosNone;
   ti.kmax = kPosMin;
+  ti.pos0 = 0;
+  ti.ss = 0;
+  ti.kp = nullptr;
+  ti.vp = nullptr;
   return ti;
 }
+
+// Key and value row addresses and position of tile row r; false past the last key.
+template <int MODE, int ELEM>
+__device__ __forceinline__ bool row_of(const Params& p, const TileInfo& ti, int r, int b, int hk,
+                                       const char*& krow, const char*& vrow, int& pos) {
+  const int64_t j = (int64_t)ti.t * BN + r;
+  if ((ti.flags & 2) && j >= p.Lk) return false;
+  if (ti.flags & 1) {
+    krow = ti.kp + (int64_t)r * ti.ss * ELEM;
+    vrow = ti.vp + (int64_t)r * ti.ss * ELEM;
+    pos = ti.pos0 + r;
+    return true;
+  }
+  int c = ti.cursor;
+  ChunkDev ch = chunk_at<MODE>(p, c);
+  while (c + 1 < p.n_chunks && j >= ch.start + ch.len) {
+    ++c;
+    ch = chunk_at<MODE>(p, c);
+  }
+  const int64_t off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j - ch.start) * ch.ss;
+  krow = (const char*)ch.k + off * ELEM;
+  vrow = (const char*)ch.v + off * ELEM;
+  pos = ch.pos0 + (int)(j - ch.start);
+  return true;
+}
+
+// True when every row of the tile comes from one chunk, none lies past the last
+// key, and rows are 16-byte aligned runs of exactly `dp` elements: then the
+// tile can be fetched with unconditional vector loads (a uniform condition).
+__device__ __forceinline__ bool fast_tile(const Params& p, const TileInfo& ti, int dp) {
+  return ti.flags == 1 && p.vec && p.d == dp;
+}
+
+// ---------------------------------------------------------------------------
+// Element-type specific pieces: LDS layout, tile staging, MFMA fragments.
+
+template <class T, int DP>
+struct Ops;
+
+// bf16: K row-major [BN][DP + 8]; V transposed [DP][BN + 8] with the key order of
+// each 16-key slice permuted (quads 1 and 2 swapped) to match the P fragments,
+// followed by the BN key positions of the tile.
+template <int DP>
+struct Ops<__bf16, DP> {
+  static constexpr int KP = DP + 8;
+  static constexpr int VP = BN + 8;
+  static constexpr int K_BYTES = BN * KP * 2;
+  static constexpr int V_BYTES = DP * VP * 2 + BN * 4;
+  static constexpr int POS_OFF = DP * VP * 2;
+  static constexpr int CPR = DP / 8;                                     // 16-byte chunks per row
+  static constexpr int NK = (BN * CPR + kThreads - 1) / kThreads;        // K items per thread
+  static constexpr int NV = ((BN / 4) * CPR + kThreads - 1) / kThreads;  // V quad items per thread
+  static constexpr int QF = DP / 16;
+
+  struct StageK {
+    u32x4 k[NK];
+  };
+  struct StageV {
+    u32x4 v[NV][4];
+    int pos[NV][4];
+  };
+  struct QFrag {
+    bf16x8 f[QF];
+  };
+
+  static __device__ __forceinline__ u32x4 load16(const __bf16* row, int c0, int d, bool vec) {
+    if (vec) {
+      if (c0 < d) return gload16(row + c0);
+      return u32x4{0, 0, 0, 0};
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = (c0 + 2 * i < d) ? gload_u16(row + c0 + 2 * i) : 0u;
+      uint32_t hi = (c0 + 2 * i + 1 < d) ? gload_u16(row + c0 + 2 * i + 1) : 0u;
+      w[i] = lo | (hi << 16);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+  }
+
+  static __device__ __forceinline__ void load_q(const Params& p, const __bf16* qrow, bool valid, int h,
+                                                QFrag& q) {
+#pragma unroll
+    for (int kk = 0; kk < QF; ++kk) {
+      u32x4 x = valid ? load16(qrow, kk * 16 + h * 8, p.d, p.vec) : u32x4{0, 0, 0, 0};
+      q.f[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // Raw scores <q, k> of the tile, transposed: s[kb][r] is key kb*32 + 8(r/4) + 4h + r%4.
+  static __device__ __forceinline__ void qk(const char* kbuf, const QFrag& q, f32x16* s, int lane) {
+    const __bf16* base = (const __bf16*)kbuf + (lane & 31) * KP + (lane >> 5) * 8;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < QF; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        bf16x8 a = *(const bf16x8*)(base + kb * 32 * KP + kk * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.f[kk], s[kb], 0, 0, 0);
+      }
+    }
+  }
+
+  // o[db] += V^T P^T over the tile, P taken from the exponentiated score blocks.
+  static __device__ __forceinline__ void pv(const char* vbuf, const f32x16* s, f32x16* o, int lane) {
+    const __bf16* Vs = (const __bf16*)vbuf;
+    bf16x8 pf[BN / 16];
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pf[ks][t] = (__bf16)s[ks >> 1][(ks & 1) * 8 + t];
+    }
+    const __bf16* vrow = Vs + (lane & 31) * VP + (lane >> 5) * 8;
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db) {
+        bf16x8 a = *(const bf16x8*)(vrow + db * 32 * VP + ks * 16);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  template <int MODE>
+  static __device__ __forceinline__ void fetch_k(const Params& p, const TileInfo& ti, int b, int hk, int tid,
+                                                 StageK& st) {
+    if (fast_tile(p, ti, DP)) {
+      // one chunk, no tail, aligned rows of exactly DP elements: straight-line loads
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int item = tid + i * kThreads;
+        if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
+          const int r = item / CPR, cc = item % CPR;
+          st.k[i] = gload16(ti.kp + ((int64_t)r * ti.ss + cc * 8) * 2);
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int item = tid + i * kThreads;
+      st.k[i] = u32x4{0, 0, 0, 0};
+      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
+        const int r = item / CPR, cc = item % CPR;
+        const char *kr, *vr;
+        int pos;
+        if (row_of<MODE, 2>(p, ti, r, b, hk, kr, vr, pos)) st.k[i] = load16((const __bf16*)kr, cc * 8, p.d, p.vec);
+      }
+    }
+  }
+
+  template <int MODE>
+  static __device__ __forceinline__ void fetch_v(const Params& p, const TileInfo& ti, int b, int hk, int tid,
+                                                 StageV& st) {
+    if (fast_tile(p, ti, DP)) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int item = tid + i * kThreads;
+        if (((BN / 4) * CPR) % kThreads == 0 || item < (BN / 4) * CPR) {
+          const int qd = item % (BN / 4), cc = item / (BN / 4);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            st.v[i][w] = gload16(ti.vp + ((int64_t)(qd * 4 + w) * ti.ss + cc * 8) * 2);
+            st.pos[i][w] = ti.pos0 + qd * 4 + w;
+          }
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int item = tid + i * kThreads;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        st.v[i][w] = u32x4{0, 0, 0, 0};
+        st.pos[i][w] = kPosNone;
+      }
+      if (((BN / 4) * CPR) % kThreads == 0 || item < (BN / 4) * CPR) {
+        const int qd = item % (BN / 4), cc = item / (BN / 4);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const char *kr, *vr;
+          int pos;
+          if (row_of<MODE, 2>(p, ti, qd * 4 + w, b, hk, kr, vr, pos)) {
+            st.v[i][w] = load16((const __bf16*)vr, cc * 8, p.d, p.vec);
+            st.pos[i][w] = pos;
+          }
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void store_k(char* kbuf, const StageK& st, int tid) {
+    __bf16* Ks = (__bf16*)kbuf;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int item = tid + i * kThreads;
+      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
+        const int r = item / CPR, cc = item % CPR;
+        *(u32x4*)(Ks + r * KP + cc * 8) = st.k[i];
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void store_v(char* vbuf, const StageV& st, int tid) {
+    __bf16* Vs = (__bf16*)vbuf;
+    int* P = (int*)(vbuf + POS_OFF);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int item = tid + i * kThreads;
+      if (((BN / 4) * CPR) % kThreads == 0 || item < (BN / 4) * CPR) {
+        const int qd = item % (BN / 4), cc = item / (BN / 4);
+        const int qi = qd & 3;
+        const int pq = (qd & ~3) | (qi == 1 ? 2 : (qi == 2 ? 1 : qi));
+        const u32x4* r = st.v[i];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // dword w of each key row holds d = 2w (low half) and d = 2w + 1 (high half)
+          const uint32_t e0 = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
+          const uint32_t e1 = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
+          const uint32_t o0 = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
+          const uint32_t o1 = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
+          *(u32x2*)(Vs + (cc * 8 + 2 * w) * VP + pq * 4) = u32x2{e0, e1};
+          *(u32x2*)(Vs + (cc * 8 + 2 * w + 1) * VP + pq * 4) = u32x2{o0, o1};
+        }
+        if (cc == 0) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) P[qd * 4 + w] = st.pos[i][w];
+        }
+      }
+    }
+  }
+};
+
+// fp32: K and V both row-major [BN][DP + 4] (V followed by the key positions);
+// fragments for v_mfma_f32_32x32x2f32.
+template <int DP>
+struct Ops<float, DP> {
+  static constexpr int KP = DP + 4;
+  static constexpr int K_BYTES = BN * KP * 4;
+  static constexpr int V_BYTES = BN * KP * 4 + BN * 4;
+  static constexpr int POS_OFF = BN * KP * 4;
+  static constexpr int CPR = DP / 4;
+  static constexpr int NK = (BN * CPR + kThreads - 1) / kThreads;
+  static constexpr int QF = DP / 2;
+
+  struct StageK {
+    u32x4 k[NK];
+  };
+  struct StageV {
+    u32x4 v[NK];
+    int pos[NK];
+  };
+  struct QFrag {
+    float f[QF];
+  };
+
+  static __device__ __forceinline__ u32x4 load16(const float* row, int c0, int d, bool vec) {
+    if (vec) {
+      if (c0 < d) return gload16(row + c0);
+      return u32x4{0, 0, 0, 0};
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (c0 + i < d) ? __float_as_uint(gload_f32(row + c0 + i)) : 0u;
+    return u32x4{w[0], w[1], w[2], w[3]};
+  }
+
+  static __device__ __forceinline__ void load_q(const Params& p, const float* qrow, bool valid, int h,
+                                                QFrag& q) {
+#pragma unroll
+    for (int kk = 0; kk < QF; ++kk) {
+      const int c = 2 * kk + h;
+      q.f[kk] = (valid && c < p.d) ? gload_f32(qrow + c) : 0.f;
+    }
+  }
+
+  static __device__ __forceinline__ void qk(const char* kbuf, const QFrag& q, f32x16* s, int lane) {
+    const float* base = (const float*)kbuf + (lane & 31) * KP + (lane >> 5);
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < QF; ++kk)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(base[kb * 32 * KP + 2 * kk], q.f[kk], s[kb], 0, 0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ void pv(const char* vbuf, const f32x16* s, f32x16* o, int lane) {
+    const float* Vs = (const float*)vbuf;
+    const int h = lane >> 5;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+        for (int db = 0; db < DP / 32; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * KP + db * 32 + (lane & 31)], s[kb][r], o[db], 0,
+                                                       0, 0);
+      }
+    }
+  }
+
+  template <int MODE>
+  static __device__ __forceinline__ void fetch_k(const Params& p, const TileInfo& ti, int b, int hk, int tid,
+                                                 StageK& st) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int item = tid + i * kThreads;
+      st.k[i] = u32x4{0, 0, 0, 0};
+      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
+        const int r = item / CPR, cc = item % CPR;
+        const char *kr, *vr;
+        int pos;
+        if (row_of<MODE, 4>(p, ti, r, b, hk, kr, vr, pos)) st.k[i] = load16((const float*)kr, cc * 4, p.d, p.vec);
+      }
+    }
+  }
+
+  template <int MODE>
+  static __device__ __forceinline__ void fetch_v(const Params& p, const TileInfo& ti, int b, int hk, int tid,
+                                                 StageV& st) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int item = tid + i * kThreads;
+      st.v[i] = u32x4{0, 0, 0, 0};
+      st.pos[i] = kPosNone;
+      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
+        const int r = item / CPR, cc = item % CPR;
+        const char *kr, *vr;
+        int pos;
+        if (row_of<MODE, 4>(p, ti, r, b, hk, kr, vr, pos)) {
+          st.v[i] = load16((const float*)vr, cc * 4, p.d, p.vec);
+          st.pos[i] = pos;
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void store_k(char* kbuf, const StageK& st, int tid) {
+    float* Ks = (float*)kbuf;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int item = tid + i * kThreads;
+      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
+        const int r = item / CPR, cc = item % CPR;
+        *(u32x4*)(Ks + r * KP + cc * 4) = st.k[i];
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void store_v(char* vbuf, const StageV& st, int tid) {
+    float* Vs = (float*)vbuf;
+    int* P = (int*)(vbuf + POS_OFF);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int item = tid + i * kThreads;
+      if ((BN * CPR) % kThreads == 0 || item < BN * CPR) {
+        const int r = item / CPR, cc = item % CPR;
+        *(u32x4*)(Vs + r * KP + cc * 4) = st.v[i];
+        if (cc == 0) P[r] = st.pos[i];
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int query_pos(const Params& p, int64_t row) {
   for (int s = 0; s < p.n_qseg; ++s) {
@@ -506,10 +589,21 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
+// Per-wave view of a tile: 0 = nothing visible, 1 = everything visible, 2 = mixed.
+__device__ __forceinline__ int wave_mode(const TileInfo& ti, int wqmin, int wqmax, bool causal) {
+  if (causal) {
+    if (ti.kmin > wqmax) return 0;
+    if ((ti.flags & 2) || ti.kmax > wqmin) return 2;
+    return 1;
+  }
+  return (ti.flags & 2) ? 2 : 1;
+}
+
 template <class T, int DP, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   using O = Ops<T, DP>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * O::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) char kbuf[2][O::K_BYTES];
+  __shared__ __attribute__((aligned(16))) char vbuf[2][O::V_BYTES];
   __shared__ int qred[2 * kWaves];
 
   const int tid = threadIdx.x;
@@ -519,8 +613,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
 
   // Work decode. Blocks are dealt to the 8 XCDs round-robin; remap so that each
   // XCD gets a contiguous range of work items, and order items so that the
-  // blocks sharing one key/value head (all q tiles of a head, and all query
-  // heads of a GQA group) are adjacent and share that XCD's L2.
+  // blocks sharing one key/value head and key range (all query tiles of a head,
+  // and all query heads of a GQA group) are adjacent and share that XCD's L2.
   int w = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) w = (w & 7) * (nwg >> 3) + (w >> 3);
@@ -529,6 +623,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   w /= group;
   int qt = w % p.n_qt;
   w /= p.n_qt;
+  const int split = w % p.nsplit;
+  w /= p.nsplit;
   const int hk = w % p.Hkv;
   const int b = w / p.Hkv;
   if (MODE == kRingCausal) qt = p.n_qt - 1 - qt;  // later queries see more keys: start them first
@@ -536,15 +632,15 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
 
   const int64_t row = (int64_t)qt * BM + wave * 32 + (lane & 31);
   const bool valid = row < p.Lq;
-  const int64_t qoff = (((int64_t)b * p.Hq + hq) * p.Lq + (valid ? row : 0)) * p.d;
+  const int64_t qrow_idx = ((int64_t)b * p.Hq + hq) * p.Lq + (valid ? row : 0);
 
   // Query positions and their bounds per wave and per workgroup.
   int qpos = kPosAll;
   int wqmin = kPosAll, wqmax = kPosAll, gqmax = kPosAll;
   if (MODE == kRingCausal) {
     qpos = valid ? query_pos(p, row) : kPosMin;
-    wqmin = wave_min(valid ? qpos : kPosNone);
-    wqmax = wave_max(valid ? qpos : kPosMin);
+    wqmin = __builtin_amdgcn_readfirstlane(wave_min(valid ? qpos : kPosNone));
+    wqmax = __builtin_amdgcn_readfirstlane(wave_max(valid ? qpos : kPosMin));
     if (lane == 0) {
       qred[wave] = wqmin;
       qred[kWaves + wave] = wqmax;
@@ -556,7 +652,10 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   }
 
   typename O::QFrag qf;
-  O::load_q(p, (const T*)p.q + qoff, valid, h, qf);
+  O::load_q(p, (const T*)p.q + qrow_idx * p.d, valid, h, qf);
+  // Drain the query loads here, once: otherwise the wait-count analysis carries
+  // them into the tile loop and drains every HBM prefetch at each tile.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
   f32x16 o[DP / 32];
 #pragma unroll
@@ -564,86 +663,111 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   float m_run = -INFINITY;  // running max of raw dot products <q, k>
   float l_run = 0.f;        // this lane's share of the running denominator
 
-  const int64_t ntiles = (p.Lk + BN - 1) / BN;
-  typename O::Stage st;
-  TileInfo cur = next_tile<MODE>(p, 0, 0, ntiles, gqmax);
-  if (cur.t < ntiles) {
-    O::template fetch<MODE>(p, cur.t * BN, cur.cursor, cur.one_chunk, b, hk, tid, st);
-    O::store(smem, st, tid);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (cur.t < ntiles) {
-    TileInfo nxt = next_tile<MODE>(p, cur.t + 1, cur.cursor, ntiles, gqmax);
-    if (nxt.t < ntiles) O::template fetch<MODE>(p, nxt.t * BN, nxt.cursor, nxt.one_chunk, b, hk, tid, st);
+  // This workgroup's key tiles: range `split` of nsplit equal ranges.
+  const int ntiles = (int)((p.Lk + BN - 1) / BN);
+  const int tbeg = (int)((int64_t)ntiles * split / p.nsplit);
+  const int tend = (int)((int64_t)ntiles * (split + 1) / p.nsplit);
+  constexpr int ELEM = sizeof(T);
 
-    // Per-wave view of the tile: nothing visible, everything visible, or mixed.
-    bool skip = false, masked = cur.tail;
-    if (MODE == kRingCausal) {
-      skip = cur.kmin > wqmax;
-      masked = masked || cur.kmax > wqmin;
-    }
-    if (!skip) {
-      const char* tb = smem + buf * O::BUF_BYTES;
-      f32x16 s[BN / 32];
+  typename O::StageK sk;
+  typename O::StageV sv;
+  f32x16 s0[BN / 32];
+
+  // Softmax of one tile (its raw scores in s), folded into the running state,
+  // then O += P V with the tile's V from LDS.
+  auto consume = [&](f32x16* s, int mode, const char* vb_) {
+    if (mode == 2) {
+      const int* kp = (const int*)(vb_ + O::POS_OFF);
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) s[kb] = O::qk(tb, qf, kb, lane);
-      if (masked) {
-        const int* kp = (const int*)(tb + O::K_BYTES + O::V_BYTES);
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (kp[key] > qpos) s[kb][r] = -INFINITY;
-          }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = fmaxf(mt, wave_xor32(mt));
-      const float mnew = fmaxf(m_run, mt);
-      const float ms = (mnew == -INFINITY) ? 0.f : mnew * p.c2;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * p.c2 - ms);
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int k2 = 0; k2 < BN / 32; ++k2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c2, -ms));
-          s[kb][r] = e;
-          rs += e;
+          const int key = k2 * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (kp[key] > qpos) s[k2][r] = -INFINITY;
         }
-      l_run = fmaf(l_run, alpha, rs);
-      m_run = mnew;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DP / 32; ++db) o[db] *= alpha;
-      }
-      O::pv(tb, s, o, lane);
     }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int k2 = 0; k2 < BN / 32; ++k2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[k2][r], s[k2][r + 1]));
+    mt = fmaxf(mt, wave_xor32(mt));
+    const float mnew = fmaxf(m_run, mt);
+    const float ms = (mnew == -INFINITY) ? 0.f : mnew * p.c2;
+    const float alpha = __builtin_amdgcn_exp2f(m_run * p.c2 - ms);
+    float rs = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < BN / 32; ++k2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[k2][r], p.c2, -ms));
+        s[k2][r] = e;
+        rs += e;
+      }
+    l_run = fmaf(l_run, alpha, rs);
+    m_run = mnew;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db) o[db] *= alpha;
+    }
+    __builtin_amdgcn_s_setprio(1);
+    O::pv(vb_, s, o, lane);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-    if (nxt.t < ntiles) O::store(smem + (buf ^ 1) * O::BUF_BYTES, st, tid);
-    __syncthreads();
-    buf ^= 1;
+  // K and V of a tile are staged together; the tile after is fetched from HBM
+  // into registers while this one is computed.
+  TileInfo cur = next_tile<MODE, ELEM>(p, tbeg, 0, tend, gqmax, b, hk);
+  if (cur.t < tend) {
+    O::template fetch_k<MODE>(p, cur, b, hk, tid, sk);
+    O::template fetch_v<MODE>(p, cur, b, hk, tid, sv);
+    O::store_k(kbuf[0], sk, tid);
+    O::store_v(vbuf[0], sv, tid);
+  }
+  int bi = 0;
+  while (cur.t < tend) {
+    const TileInfo nxt = next_tile<MODE, ELEM>(p, cur.t + 1, cur.cursor, tend, gqmax, b, hk);
+    if (nxt.t < tend) {
+      O::template fetch_k<MODE>(p, nxt, b, hk, tid, sk);
+      O::template fetch_v<MODE>(p, nxt, b, hk, tid, sv);
+    }
+    __syncthreads();  // K(cur) and V(cur) are in LDS
+    const int mode = wave_mode(cur, wqmin, wqmax, MODE == kRingCausal);
+    if (mode) {
+      // Raised priority while issuing matrix ops: of the two waves sharing a
+      // SIMD, the one with MFMAs ready goes first and the other fills VALU slots.
+      __builtin_amdgcn_s_setprio(1);
+      O::qk(kbuf[bi], qf, s0, lane);
+      __builtin_amdgcn_s_setprio(0);
+      consume(s0, mode, vbuf[bi]);
+    }
+    if (nxt.t < tend) {
+      O::store_k(kbuf[bi ^ 1], sk, tid);
+      O::store_v(vbuf[bi ^ 1], sv, tid);
+    }
+    bi ^= 1;
     cur = nxt;
   }
 
   // Epilogue: combine the two half-waves' denominators, then write.
   const float l = l_run + wave_xor32(l_run);
   if (!valid) return;
-  float* orow = p.o + qoff;
+  float* orow;
   float inv = 1.f;
-  if (MODE != kStats) inv = (l > 0.f) ? 1.f / l : 0.f;
+  if (p.nsplit > 1) {
+    const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
+    orow = p.part + ((int64_t)split * rows + qrow_idx) * p.d;
+  } else {
+    orow = p.o + qrow_idx * p.d;
+    if (MODE != kStats) inv = (l > 0.f) ? 1.f / l : 0.f;
+  }
 #pragma unroll
   for (int db = 0; db < DP / 32; ++db) {
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       const int c0 = db * 32 + 8 * gi + 4 * h;
-      f32x4 v = {o[db][4 * gi] * inv, o[db][4 * gi + 1] * inv, o[db][4 * gi + 2] * inv,
-                 o[db][4 * gi + 3] * inv};
+      const f32x4 v = {o[db][4 * gi] * inv, o[db][4 * gi + 1] * inv, o[db][4 * gi + 2] * inv,
+                       o[db][4 * gi + 3] * inv};
       if (c0 + 3 < p.d && (p.d & 3) == 0) {
         *(f32x4*)(orow + c0) = v;
       } else {
@@ -654,15 +778,47 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
     }
   }
   if (h == 0) {
-    const int64_t ri = ((int64_t)b * p.Hq + hq) * p.Lq + row;
-    const float m_out = (m_run == -INFINITY) ? -INFINITY : m_run * p.scale;
-    if (MODE == kStats) {
-      p.l[ri] = l;
-      p.m[ri] = m_out;
-    } else if (p.l != nullptr) {
-      p.l[ri] = (l > 0.f) ? m_out + logf(l) : -INFINITY;
+    if (p.nsplit > 1) {
+      const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
+      float* pl = p.part + (int64_t)p.nsplit * rows * p.d;
+      pl[(int64_t)split * rows + qrow_idx] = l;
+      pl[((int64_t)p.nsplit + split) * rows + qrow_idx] = m_run;  // raw units
+    } else {
+      const float m_out = (m_run == -INFINITY) ? -INFINITY : m_run * p.scale;
+      if (MODE == kStats) {
+        p.l[qrow_idx] = l;
+        p.m[qrow_idx] = m_out;
+      } else if (p.l != nullptr) {
+        p.l[qrow_idx] = (l > 0.f) ? m_out + logf(l) : -INFINITY;
+      }
     }
   }
+}
+
+// Merge of the key-range partials of each row, in range order, then u / l.
+// Each row is handled by LPR lanes of one wave.
+__global__ __launch_bounds__(256) void combine_kernel(int64_t rows, int d, int nsplit, int lpr, int lpr_shift,
+                                                      const float* __restrict__ part, float* __restrict__ out,
+                                                      float* __restrict__ lse, float c2, float scale) {
+  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> lpr_shift;
+  if (r >= rows) return;
+  const int sub = threadIdx.x & (lpr - 1);
+  const float* pl = part + (int64_t)nsplit * rows * d;
+  const float* pm = pl + (int64_t)nsplit * rows;
+  float mx = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pm[(int64_t)s * rows + r]);
+  const float ms = (mx == -INFINITY) ? 0.f : mx * c2;
+  float l = 0.f;
+  for (int s = 0; s < nsplit; ++s)
+    l = fmaf(pl[(int64_t)s * rows + r], __builtin_amdgcn_exp2f(pm[(int64_t)s * rows + r] * c2 - ms), l);
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  for (int c = sub; c < d; c += lpr) {
+    float u = 0.f;
+    for (int s = 0; s < nsplit; ++s)
+      u = fmaf(part[((int64_t)s * rows + r) * d + c], __builtin_amdgcn_exp2f(pm[(int64_t)s * rows + r] * c2 - ms), u);
+    out[r * d + c] = u * inv;
+  }
+  if (sub == 0 && lse != nullptr) lse[r] = (l > 0.f) ? mx * scale + logf(l) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -694,7 +850,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int64_t rows, int d, int lpr
       f32x4* pa = (f32x4*)(au + r * d);
       const f32x4* pb = (const f32x4*)(bu + r * d);
       for (int c = sub; c < n4; c += lpr) {
-        f32x4 x = pa[c], y = pb[c];
+        const f32x4 x = pa[c], y = pb[c];
         pa[c] = x * fa + y * fb;
       }
     } else {
@@ -723,9 +879,7 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int hip_fail(hipError_t e, const char* what) {
-  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
-}
+int hip_fail(hipError_t e, const char* what) { return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e)); }
 
 constexpr int64_t kPosLimit = 0x7ffffffeLL;
 
@@ -735,12 +889,11 @@ int check_dims(int dtype, int batch, int q_heads, int kv_heads, int head_dim) {
     return fail(RA_ERR_SHAPE, "batch=%d q_heads=%d kv_heads=%d", batch, q_heads, kv_heads);
   if (q_heads % kv_heads != 0)
     return fail(RA_ERR_SHAPE, "q_heads=%d is not a multiple of kv_heads=%d", q_heads, kv_heads);
-  if (head_dim < 1 || head_dim > 128)
-    return fail(RA_ERR_UNSUPPORTED, "head_dim=%d outside 1..128", head_dim);
+  if (head_dim < 1 || head_dim > 128) return fail(RA_ERR_UNSUPPORTED, "head_dim=%d outside 1..128", head_dim);
   return RA_OK;
 }
 
-int check_chunk(const ra_kv_chunk& c, int idx, int batch, int kv_heads, int head_dim, int64_t elem) {
+int check_chunk(const ra_kv_chunk& c, int idx, int head_dim) {
   if (c.len < 0) return fail(RA_ERR_SHAPE, "chunk %d: negative length", idx);
   if (c.len == 0) return RA_OK;
   if (!c.k || !c.v) return fail(RA_ERR_NULL, "chunk %d: null k or v", idx);
@@ -750,9 +903,6 @@ int check_chunk(const ra_kv_chunk& c, int idx, int batch, int kv_heads, int head
   if (c.stride_s < head_dim || c.stride_b < 0 || c.stride_h < 0)
     return fail(RA_ERR_SHAPE, "chunk %d: strides b=%lld h=%lld s=%lld invalid for head_dim %d", idx,
                 (long long)c.stride_b, (long long)c.stride_h, (long long)c.stride_s, head_dim);
-  (void)batch;
-  (void)kv_heads;
-  (void)elem;
   return RA_OK;
 }
 
@@ -761,7 +911,28 @@ bool vec_ok(const void* p, int64_t stride, int head_dim, int64_t elem) {
   return ((uintptr_t)p % 16 == 0) && stride % per16 == 0 && head_dim % per16 == 0;
 }
 
+bool chunk_vec_ok(const ra_kv_chunk& c, int head_dim, int64_t elem) {
+  if (c.len == 0) return true;
+  const int64_t per16 = 16 / elem;
+  return vec_ok(c.k, c.stride_s, head_dim, elem) && vec_ok(c.v, c.stride_s, head_dim, elem) &&
+         c.stride_b % per16 == 0 && c.stride_h % per16 == 0;
+}
+
 int dp_of(int head_dim) { return head_dim <= 32 ? 32 : (head_dim <= 64 ? 64 : 128); }
+
+// Key-range split for grids that cannot fill the chip: depends only on the
+// shape (never on the chunk list), so every split of a sequence into chunks
+// runs the same arithmetic.
+int choose_nsplit(int64_t base_blocks, int64_t lk) {
+  const int64_t ntiles = (lk + BN - 1) / BN;
+  const int64_t target = 1024;  // 256 CUs x 2 resident workgroups x 2 rounds
+  if (base_blocks >= target / 2) return 1;
+  int64_t s = (target + base_blocks - 1) / base_blocks;
+  const int64_t max_by_work = ntiles / 16;  // keep at least 16 tiles per range
+  if (s > max_by_work) s = max_by_work;
+  if (s > 32) s = 32;
+  return s < 1 ? 1 : (int)s;
+}
 
 template <class T, int DP, int MODE>
 hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
@@ -789,6 +960,14 @@ hipError_t launch(int mode, int dtype, int dp, const Params& p, int nblocks, hip
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+size_t table_bytes(int n_chunks, int n_q_segments) {
+  return align256(sizeof(ChunkDev) * (size_t)n_chunks) + align256(sizeof(QSegDev) * (size_t)n_q_segments);
+}
+
+size_t partial_bytes(int nsplit, int64_t rows, int head_dim) {
+  return nsplit > 1 ? align256(sizeof(float) * (size_t)nsplit * (size_t)rows * (size_t)(head_dim + 2)) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -808,15 +987,21 @@ const char* ra_status_string(int status) {
 
 const char* ra_last_error(void) { return g_err; }
 
-size_t ra_ring_workspace_bytes(int n_chunks, int n_q_segments) {
+size_t ra_ring_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys,
+                               int n_chunks, int n_q_segments) {
   if (n_chunks < 0) n_chunks = 0;
   if (n_q_segments < 0) n_q_segments = 0;
-  return align256(sizeof(ChunkDev) * (size_t)n_chunks) + align256(sizeof(QSegDev) * (size_t)n_q_segments) + 256;
+  size_t bytes = table_bytes(n_chunks, n_q_segments) + 256;
+  if (batch > 0 && q_heads > 0 && q_len > 0 && head_dim > 0 && total_keys > 0) {
+    const int64_t base = ((q_len + BM - 1) / BM) * (int64_t)q_heads * batch;
+    bytes += partial_bytes(choose_nsplit(base, total_keys), (int64_t)batch * q_heads * q_len, head_dim);
+  }
+  return bytes;
 }
 
-int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, int head_dim,
-                             const void* q, int64_t q_len, const ra_kv_chunk* chunk, float scale,
-                             float* u, float* l, float* m, void* stream) {
+int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
+                             int64_t q_len, const ra_kv_chunk* chunk, float scale, float* u, float* l, float* m,
+                             void* stream) {
   g_err[0] = 0;
   int st = check_dims(dtype, batch, q_heads, kv_heads, head_dim);
   if (st) return st;
@@ -824,7 +1009,7 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   if (q_len < 0) return fail(RA_ERR_SHAPE, "q_len=%lld", (long long)q_len);
   if (!(scale > 0.f) || !isfinite(scale)) return fail(RA_ERR_SHAPE, "scale must be finite and > 0");
   const int64_t elem = dtype == RA_BF16 ? 2 : 4;
-  if ((st = check_chunk(*chunk, 0, batch, kv_heads, head_dim, elem))) return st;
+  if ((st = check_chunk(*chunk, 0, head_dim))) return st;
   if (q_len == 0 || batch == 0) return RA_OK;
   if (!q || !u || !l || !m) return fail(RA_ERR_NULL, "q, u, l and m must be non-null");
   if (chunk->len > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "chunk longer than 2^31-2 keys");
@@ -854,19 +1039,17 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.Hkv = kv_heads;
   p.d = head_dim;
   p.n_qt = (int)n_qt;
-  p.vec = vec_ok(q, head_dim, head_dim, elem) &&
-          (chunk->len == 0 || (vec_ok(chunk->k, chunk->stride_s, head_dim, elem) &&
-                               vec_ok(chunk->v, chunk->stride_s, head_dim, elem) &&
-                               chunk->stride_b % (16 / elem) == 0 && chunk->stride_h % (16 / elem) == 0));
+  p.nsplit = 1;
+  p.vec = vec_ok(q, head_dim, head_dim, elem) && chunk_vec_ok(*chunk, head_dim, elem);
   p.scale = scale;
-  p.c2 = scale * 1.4426950408889634f;
+  p.c2 = scale * kLog2e;
   hipError_t e = launch(kStats, dtype, dp_of(head_dim), p, (int)nblocks, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention_chunk_stats launch");
   return RA_OK;
 }
 
-int ra_merge_chunk_stats(int64_t rows, int head_dim, float* acc_u, float* acc_l, float* acc_m,
-                         const float* u, const float* l, const float* m, void* stream) {
+int ra_merge_chunk_stats(int64_t rows, int head_dim, float* acc_u, float* acc_l, float* acc_m, const float* u,
+                         const float* l, const float* m, void* stream) {
   g_err[0] = 0;
   if (rows < 0) return fail(RA_ERR_SHAPE, "rows=%lld", (long long)rows);
   if (head_dim < 1) return fail(RA_ERR_SHAPE, "head_dim=%d", head_dim);
@@ -895,9 +1078,9 @@ int ra_merge_chunk_stats(int64_t rows, int head_dim, float* acc_u, float* acc_l,
 }
 
 int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
-                      const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks,
-                      int n_chunks, int causal, float scale, void* workspace, size_t workspace_bytes,
-                      float* out, float* lse, void* stream) {
+                      const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks, int n_chunks,
+                      int causal, float scale, void* workspace, size_t workspace_bytes, float* out, float* lse,
+                      void* stream) {
   g_err[0] = 0;
   int st = check_dims(dtype, batch, q_heads, kv_heads, head_dim);
   if (st) return st;
@@ -916,31 +1099,30 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   int64_t lk = 0;
   bool vec = true;
   for (int c = 0; c < n_chunks; ++c) {
-    if ((st = check_chunk(chunks[c], c, batch, kv_heads, head_dim, elem))) return st;
+    if ((st = check_chunk(chunks[c], c, head_dim))) return st;
     lk += chunks[c].len;
-    if (chunks[c].len > 0)
-      vec = vec && vec_ok(chunks[c].k, chunks[c].stride_s, head_dim, elem) &&
-            vec_ok(chunks[c].v, chunks[c].stride_s, head_dim, elem) &&
-            chunks[c].stride_b % (16 / elem) == 0 && chunks[c].stride_h % (16 / elem) == 0;
+    vec = vec && chunk_vec_ok(chunks[c], head_dim, elem);
   }
   if (lk > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "more than 2^31-2 keys in total");
   if (lq == 0 || batch == 0) return RA_OK;
   if (!q || !out) return fail(RA_ERR_NULL, "q and out must be non-null");
-  const size_t need = ra_ring_workspace_bytes(n_chunks, n_q_segments);
-  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0)
-    return fail(RA_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-                workspace_bytes);
   const int64_t n_qt = (lq + BM - 1) / BM;
-  const int64_t nblocks = n_qt * q_heads * batch;
+  const int64_t base_blocks = n_qt * q_heads * batch;
+  const int nsplit = lk > 0 ? choose_nsplit(base_blocks, lk) : 1;
+  const int64_t nblocks = base_blocks * nsplit;
   if (nblocks > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
+  const int64_t rows = (int64_t)batch * q_heads * lq;
+  const size_t tbytes = table_bytes(n_chunks, n_q_segments);
+  const size_t need = ra_ring_workspace_bytes(batch, q_heads, head_dim, lq, lk, n_chunks, n_q_segments);
+  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0)
+    return fail(RA_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, workspace_bytes);
 
   // Descriptor tables: chunks (non-empty ones only; order kept) then query segments.
-  const size_t cbytes = align256(sizeof(ChunkDev) * (size_t)n_chunks);
-  const size_t qbytes = align256(sizeof(QSegDev) * (size_t)n_q_segments);
-  char* host = (char*)calloc(1, cbytes + qbytes);
+  char* host = (char*)calloc(1, tbytes > 0 ? tbytes : 1);
   if (!host) return fail(RA_ERR_UNSUPPORTED, "host allocation failed");
+  const size_t cbytes = align256(sizeof(ChunkDev) * (size_t)n_chunks);
   ChunkDev* hc = (ChunkDev*)host;
-  QSegDev* hq = (QSegDev*)(host + cbytes);
+  QSegDev* hqs = (QSegDev*)(host + cbytes);
   int nc = 0;
   int64_t start = 0;
   for (int c = 0; c < n_chunks; ++c) {
@@ -958,13 +1140,13 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   }
   int64_t row0 = 0;
   for (int s = 0; s < n_q_segments; ++s) {
-    hq[s].row0 = row0;
-    hq[s].len = q_segments[s].len;
-    hq[s].pos0 = q_segments[s].global_offset;
+    hqs[s].row0 = row0;
+    hqs[s].len = q_segments[s].len;
+    hqs[s].pos0 = q_segments[s].global_offset;
     row0 += q_segments[s].len;
   }
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(workspace, host, cbytes + qbytes, hipMemcpyHostToDevice, hs);
+  hipError_t e = hipMemcpyAsync(workspace, host, tbytes, hipMemcpyHostToDevice, hs);
   free(host);
   if (e != hipSuccess) return hip_fail(e, "ring_attention descriptor copy");
 
@@ -973,26 +1155,36 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   p.o = out;
   p.l = lse;
   p.m = nullptr;
+  p.part = nsplit > 1 ? (float*)((char*)workspace + tbytes) : nullptr;
   p.chunks = (const ChunkDev*)workspace;
   p.qsegs = (const QSegDev*)((char*)workspace + cbytes);
   p.Lq = lq;
   p.Lk = lk;
-  p.n_chunks = nc > 0 ? nc : 1;
+  p.n_chunks = nc > 0 ? nc : 1;  // with no keys the tile walk is empty and never reads the table
   p.n_qseg = n_q_segments;
   p.B = batch;
   p.Hq = q_heads;
   p.Hkv = kv_heads;
   p.d = head_dim;
   p.n_qt = (int)n_qt;
+  p.nsplit = nsplit;
   p.vec = vec && vec_ok(q, head_dim, head_dim, elem);
   p.scale = scale;
-  p.c2 = scale * 1.4426950408889634f;
-  if (nc == 0) {
-    // no keys at all: the tile walk is empty, every row ends with l = 0
-    p.chunks = (const ChunkDev*)workspace;
-  }
+  p.c2 = scale * kLog2e;
   e = launch(causal ? kRingCausal : kRingFull, dtype, dp_of(head_dim), p, (int)nblocks, hs);
   if (e != hipSuccess) return hip_fail(e, "ring_attention launch");
+  if (nsplit > 1) {
+    int lpr = 1, sh = 0;
+    while (lpr < head_dim && lpr < 64) {
+      lpr <<= 1;
+      ++sh;
+    }
+    const int64_t cblocks = (rows * lpr + 255) / 256;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)cblocks), dim3(256), 0, hs, rows, head_dim, nsplit, lpr, sh,
+                       (const float*)p.part, out, lse, p.c2, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "ring_attention combine launch");
+  }
   return RA_OK;
 }
 

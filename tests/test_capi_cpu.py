@@ -54,9 +54,16 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.ra_ring_workspace_bytes(0, 1) % 256 == 0
-    assert lib.ra_ring_workspace_bytes(64, 2) >= 64 * 64 + 2 * 24
-    assert lib.ra_ring_workspace_bytes(100, 1) > lib.ra_ring_workspace_bytes(10, 1)
+    assert lib.ra_ring_workspace_bytes(1, 8, 64, 4096, 0, 0, 1) % 256 == 0
+    assert lib.ra_ring_workspace_bytes(1, 32, 128, 8192, 65536, 64, 2) >= 64 * 64 + 2 * 24
+    assert lib.ra_ring_workspace_bytes(1, 32, 128, 8192, 65536, 100, 1) > \
+        lib.ra_ring_workspace_bytes(1, 32, 128, 8192, 65536, 10, 1)
+    # a grid too small for the chip gets room for per-key-range partials
+    small = lib.ra_ring_workspace_bytes(1, 8, 64, 4096, 32768, 8, 1)
+    assert small >= 2 * 8 * 4096 * 66 * 4
+    assert small % 256 == 0
+    big = lib.ra_ring_workspace_bytes(1, 32, 128, 8192, 65536, 8, 1)
+    assert big < 1 << 16  # enough query tiles: tables only
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
