@@ -38,7 +38,18 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-legs", action="store_true", help="skip the chunk-stats and merge legs")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="launch sequence for rocprofv3 counter passes: the workload's ring_attention, a device "
+                         "copy of COPY_BYTES, then the merge leg; prints what was launched")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR"),
+                    help="turn the counter CSVs of the three --profile-run passes into profiles/ summaries")
+    ap.add_argument("--command", default="", help="with --summarize-pmc: the command lines that made the CSVs")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30      # bytes read (and written) by the calibration copy
+MERGE_ROWS, MERGE_D = 32 * 8192, 128
+SIMD_NUM = 256 * 4
 
 
 def source_digest():
@@ -115,8 +126,135 @@ def cpu_baseline(w, q, kc, vc, offs, seconds):
     }
 
 
+def profile_run(args):
+    """Launches for counter collection; every kernel here is identified by name in the CSVs."""
+    import torch
+
+    import ring_attention_chunk_amd as ra
+    from ring_attention_chunk_amd import workloads as wl
+
+    dev = "cuda:0"
+    w = wl.config(args.config)
+    q, k, v, kc, vc = wl.generate_torch(w, dev)
+    offs = [o for o, _ in w.chunks]
+    for _ in range(args.warmup + args.steps):
+        ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    del q, k, v, kc, vc
+    # calibration: an elementwise kernel that reads COPY_BYTES and writes COPY_BYTES
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    sets = [(torch.randn(MERGE_ROWS, MERGE_D, device=dev), torch.rand(MERGE_ROWS, device=dev) + 0.5,
+             torch.randn(MERGE_ROWS, device=dev)) for _ in range(2)]
+    for _ in range(args.steps):
+        ra.merge_chunk_stats(sets[0], sets[1], inplace=True)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": w.name, "ring_attention_calls": args.warmup + args.steps,
+                      "copy_bytes": COPY_BYTES, "copy_calls": args.steps,
+                      "merge_bytes": 12 * (MERGE_D + 2) * MERGE_ROWS, "merge_calls": args.steps}))
+
+
+def _counter_rows(path):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, name_part, counter, reduce="sum"):
+    """Mean over dispatches of the kernel whose name contains name_part (skipping the first one).
+
+    Rows of one dispatch (one per hardware instance) are combined by `reduce`
+    ("sum", or "max" as the counter definitions do for GRBM_GUI_ACTIVE).
+    """
+    vals = {}
+    for r in rows:
+        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            x = float(r["Counter_Value"])
+            vals[key] = (vals.get(key, 0.0) + x) if reduce == "sum" else max(vals.get(key, x), x)
+    seq = [vals[k] for k in sorted(vals, key=lambda x: int(x))]
+    if len(seq) > 1:
+        seq = seq[1:]
+    return sum(seq) / len(seq) if seq else None, len(seq)
+
+
+def summarize_pmc(args):
+    from ring_attention_chunk_amd import workloads as wl
+
+    w = wl.config(args.config)
+    fetch, write, sq = (_counter_rows(d) for d in args.summarize_pmc)
+    copy_name = "neg_kernel"
+    attn_name = "attention_kernel"
+    f_copy, _ = _per_dispatch(fetch, copy_name, "FETCH_SIZE")
+    w_copy, _ = _per_dispatch(write, copy_name, "WRITE_SIZE")
+    f_attn, n_attn = _per_dispatch(fetch, attn_name, "FETCH_SIZE")
+    w_attn, _ = _per_dispatch(write, attn_name, "WRITE_SIZE")
+    f_merge, _ = _per_dispatch(fetch, "merge_kernel", "FETCH_SIZE")
+    w_merge, _ = _per_dispatch(write, "merge_kernel", "WRITE_SIZE")
+    # counters read KiB per dispatch; scale each by what it reads for the copy of known size
+    fs = (COPY_BYTES / 1024) / f_copy
+    ws = (COPY_BYTES / 1024) / w_copy
+    attn_bytes = f_attn * 1024 * fs + w_attn * 1024 * ws
+    merge_bytes = f_merge * 1024 * fs + w_merge * 1024 * ws
+    busy, _ = _per_dispatch(sq, attn_name, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui, _ = _per_dispatch(sq, attn_name, "GRBM_GUI_ACTIVE", reduce="max")
+    gui = gui / 8 if gui else gui  # the CSV holds the sum over the 8 XCDs
+    durs = {}
+    for r in sq:
+        if attn_name in r["Kernel_Name"]:
+            durs[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    dseq = [durs[k] for k in sorted(durs, key=int)][1:] or list(durs.values())
+    dur = sum(dseq) / len(dseq)
+    mops, _ = _per_dispatch(sq, attn_name, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    conf, _ = _per_dispatch(sq, attn_name, "SQ_LDS_BANK_CONFLICT")
+    lds_act, _ = _per_dispatch(sq, attn_name, "SQ_LDS_IDX_ACTIVE")
+    B, Hq, Hkv, d = w.batch, w.q_heads, w.kv_heads, w.head_dim
+    algo_bytes = 2 * (B * Hq * w.lq * d + 2 * B * Hkv * w.lk * d) + 4 * B * Hq * w.lq * d
+    out = {
+        "workload": w.name,
+        "kernel": attn_name,
+        "source_sha256_16": source_digest(),
+        "bytes_per_launch": int(attn_bytes),
+        "algorithmic_bytes_per_launch": algo_bytes,
+        "fetch_kib_per_launch_raw": f_attn,
+        "write_kib_per_launch_raw": w_attn,
+        "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib_raw": f_copy, "write_kib_raw": w_copy,
+                             "fetch_scale": fs, "write_scale": ws},
+        "mfma_busy_pct_of_gui_active": 100.0 * busy / (gui * SIMD_NUM) if busy and gui else None,
+        "mfma_busy_pct_of_duration_at_2p4ghz": 100.0 * busy / (dur * 2.4e9 * SIMD_NUM) if busy else None,
+        "profiled_duration_us": dur * 1e6,
+        "mfma_bf16_flops_per_launch": mops * 512 if mops else None,
+        "counted_flops_per_launch": wl.counted_flops(w),
+        "lds_bank_conflict_pct_of_lds_active": 100.0 * conf / lds_act if conf is not None and lds_act else None,
+        "merge": {"bytes_per_call_counted": int(merge_bytes), "algorithmic_bytes_per_call": 12 * (MERGE_D + 2) *
+                  MERGE_ROWS},
+        "dispatches_averaged": n_attn,
+        "commands": args.command,
+    }
+    path = os.path.join(ROOT, "profiles", f"attention_kernel_{w.name}_hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the whole share on a single MI355X and has no "
               "multi-GPU path; run it with --gpus 1.", file=sys.stderr)
@@ -128,6 +266,9 @@ def main():
     from ring_attention_chunk_amd import workloads as wl
 
     ra.load_library()
+    if args.profile_run:
+        profile_run(args)
+        return
     dev = "cuda:0"
     w = wl.config(args.config)
     q, k, v, kc, vc = wl.generate_torch(w, dev)
