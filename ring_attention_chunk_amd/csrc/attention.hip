@@ -104,6 +104,27 @@ struct Params {
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
+// IEEE maximum (NaN-propagating): lowers to v_maximum3_f32 with no operand
+// canonicalisation, unlike fmaxf.
+__device__ __forceinline__ float fmax_raw(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// max / sum of x over lanes l and l ^ 32, on every lane, via v_permlane32_swap.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lazy rescaling: the running numerator and denominator stay relative to a
+// reference maximum until a score exceeds it by more than 2^kLazy (in exp2
+// units), so most tiles need no rescale of u. u/l and ref + log(l) do not
+// depend on the reference; the chunk-stats call converts to the true maximum
+// at the end.
+constexpr float kLazy = 8.0f;
+
 // Loads through global-address-space pointers. Pointers read from the chunk
 // table carry no address space; generic (flat) loads would also count against
 // the LDS wait counter and make every LDS wait drain the HBM prefetch.
@@ -134,6 +155,7 @@ struct TileInfo {
   int kmin, kmax;  // smallest / largest global key position in the tile (causal only)
   int pos0;        // global position of the tile's first row if it lies in one chunk
   int ss;          // element stride between rows of chunk `cursor`
+  int cend;        // index in the concatenation one past the last key of chunk `cursor`
   const char* kp;  // address of the tile's first key row (batch and head applied)
   const char* vp;  // same for values
 };
@@ -185,6 +207,7 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
     ti.kmax = kmax;
     ti.pos0 = ch.pos0 + (int)(t0 - ch.start);
     ti.ss = (int)ch.ss;
+    ti.cend = (int)(ch.start + ch.len);
     ti.kp = (const char*)ch.k + off * ELEM;
     ti.vp = (const char*)ch.v + off * ELEM;
     return ti;
@@ -196,9 +219,30 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
   ti.kmax = kPosMin;
   ti.pos0 = 0;
   ti.ss = 0;
+  ti.cend = 0;
   ti.kp = nullptr;
   ti.vp = nullptr;
   return ti;
+}
+
+// The tile after `ti` in the walk. When it lies in the same chunk as `ti` (the
+// common case) it follows by scalar arithmetic, with no descriptor load.
+template <int MODE, int ELEM>
+__device__ __forceinline__ TileInfo successor(const Params& p, const TileInfo& ti, int end, int qmax, int b,
+                                              int hk) {
+  const int nt = ti.t + 1;
+  if (ti.flags == 1 && nt < end && (int64_t)(nt + 1) * BN <= ti.cend &&
+      (MODE != kRingCausal || ti.pos0 + BN <= qmax)) {
+    TileInfo n = ti;
+    n.t = nt;
+    n.pos0 = ti.pos0 + BN;
+    n.kmin = ti.kmin + BN;
+    n.kmax = ti.kmax + BN;
+    n.kp = ti.kp + (int64_t)BN * ti.ss * ELEM;
+    n.vp = ti.vp + (int64_t)BN * ti.ss * ELEM;
+    return n;
+  }
+  return next_tile<MODE, ELEM>(p, nt, ti.cursor, end, qmax, b, hk);
 }
 
 // Key and value row addresses and position of tile row r; false past the last key.
@@ -660,7 +704,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   f32x16 o[DP / 32];
 #pragma unroll
   for (int db = 0; db < DP / 32; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of raw dot products <q, k>
+  float m_ref = -INFINITY;  // reference max (raw dot products <q, k>) that u and l are relative to
+  float m_max = -INFINITY;  // true running max (the chunk-stats call reports it)
   float l_run = 0.f;        // this lane's share of the running denominator
 
   // This workgroup's key tiles: range `split` of nsplit equal ranges.
@@ -690,11 +735,19 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
 #pragma unroll
     for (int k2 = 0; k2 < BN / 32; ++k2)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[k2][r], s[k2][r + 1]));
-    mt = fmaxf(mt, wave_xor32(mt));
-    const float mnew = fmaxf(m_run, mt);
-    const float ms = (mnew == -INFINITY) ? 0.f : mnew * p.c2;
-    const float alpha = __builtin_amdgcn_exp2f(m_run * p.c2 - ms);
+      for (int r = 0; r < 16; r += 2) mt = fmax_raw(mt, fmax_raw(s[k2][r], s[k2][r + 1]));
+    mt = max_xor32(mt);
+    if constexpr (MODE == kStats) m_max = fmax_raw(m_max, mt);
+    // move the reference when a score exceeds it by more than 2^kLazy
+    const bool need = mt * p.c2 > m_ref * p.c2 + kLazy;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f((m_ref - mt) * p.c2) : 1.f;
+      if (need) m_ref = mt;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db) o[db] *= alpha;
+    }
+    const float ms = (m_ref == -INFINITY) ? 0.f : m_ref * p.c2;
     float rs = 0.f;
 #pragma unroll
     for (int k2 = 0; k2 < BN / 32; ++k2)
@@ -704,12 +757,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
         s[k2][r] = e;
         rs += e;
       }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = mnew;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < DP / 32; ++db) o[db] *= alpha;
-    }
+    l_run += rs;
     __builtin_amdgcn_s_setprio(1);
     O::pv(vb_, s, o, lane);
     __builtin_amdgcn_s_setprio(0);
@@ -726,7 +774,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   }
   int bi = 0;
   while (cur.t < tend) {
-    const TileInfo nxt = next_tile<MODE, ELEM>(p, cur.t + 1, cur.cursor, tend, gqmax, b, hk);
+    const TileInfo nxt = successor<MODE, ELEM>(p, cur, tend, gqmax, b, hk);
     if (nxt.t < tend) {
       O::template fetch_k<MODE>(p, nxt, b, hk, tid, sk);
       O::template fetch_v<MODE>(p, nxt, b, hk, tid, sv);
@@ -750,7 +798,15 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   }
 
   // Epilogue: combine the two half-waves' denominators, then write.
-  const float l = l_run + wave_xor32(l_run);
+  float l = sum_xor32(l_run);
+  if (MODE == kStats && m_max != m_ref) {
+    // report statistics relative to the true row maximum
+    const float f = __builtin_amdgcn_exp2f((m_ref - m_max) * p.c2);
+    l *= f;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db) o[db] *= f;
+    m_ref = m_max;
+  }
   if (!valid) return;
   float* orow;
   float inv = 1.f;
@@ -782,9 +838,9 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
       const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
       float* pl = p.part + (int64_t)p.nsplit * rows * p.d;
       pl[(int64_t)split * rows + qrow_idx] = l;
-      pl[((int64_t)p.nsplit + split) * rows + qrow_idx] = m_run;  // raw units
+      pl[((int64_t)p.nsplit + split) * rows + qrow_idx] = m_ref;  // raw units
     } else {
-      const float m_out = (m_run == -INFINITY) ? -INFINITY : m_run * p.scale;
+      const float m_out = (m_ref == -INFINITY) ? -INFINITY : m_ref * p.scale;
       if (MODE == kStats) {
         p.l[qrow_idx] = l;
         p.m[qrow_idx] = m_out;
