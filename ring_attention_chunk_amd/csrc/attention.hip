@@ -160,13 +160,13 @@ struct TileInfo {
   const char* vp;  // same for values
 };
 
-template <int MODE, int ELEM>
+template <int MODE, int ELEM, int TB = BN>
 __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor, int end, int qmax, int b,
                                               int hk) {
   TileInfo ti;
   while (t < end) {
-    const int64_t t0 = (int64_t)t * BN;
-    const int64_t t1 = min(t0 + (int64_t)BN, p.Lk);
+    const int64_t t0 = (int64_t)t * TB;
+    const int64_t t1 = min(t0 + (int64_t)TB, p.Lk);
     // advance the cursor to the chunk holding key t0 (zero-length chunks are passed over)
     ChunkDev ch = chunk_at<MODE>(p, cursor);
     while (cursor + 1 < p.n_chunks && t0 >= ch.start + ch.len) {
@@ -191,7 +191,7 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
       if (kmin > qmax) {
         // nothing here is visible; if the whole chunk is in the future, jump past it
         if (one && ch.pos0 > qmax) {
-          const int nt = (int)((ch.start + ch.len) / BN);
+          const int nt = (int)((ch.start + ch.len) / TB);
           t = nt > t ? nt : t + 1;
         } else {
           ++t;
@@ -202,7 +202,7 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
     const int64_t off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (t0 - ch.start) * ch.ss;
     ti.t = t;
     ti.cursor = cursor;
-    ti.flags = (one ? 1 : 0) | ((t0 + BN > p.Lk) ? 2 : 0);
+    ti.flags = (one ? 1 : 0) | ((t0 + TB > p.Lk) ? 2 : 0);
     ti.kmin = kmin;
     ti.kmax = kmax;
     ti.pos0 = ch.pos0 + (int)(t0 - ch.start);
@@ -227,29 +227,29 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
 
 // The tile after `ti` in the walk. When it lies in the same chunk as `ti` (the
 // common case) it follows by scalar arithmetic, with no descriptor load.
-template <int MODE, int ELEM>
+template <int MODE, int ELEM, int TB = BN>
 __device__ __forceinline__ TileInfo successor(const Params& p, const TileInfo& ti, int end, int qmax, int b,
                                               int hk) {
   const int nt = ti.t + 1;
-  if (ti.flags == 1 && nt < end && (int64_t)(nt + 1) * BN <= ti.cend &&
-      (MODE != kRingCausal || ti.pos0 + BN <= qmax)) {
+  if (ti.flags == 1 && nt < end && (int64_t)(nt + 1) * TB <= ti.cend &&
+      (MODE != kRingCausal || ti.pos0 + TB <= qmax)) {
     TileInfo n = ti;
     n.t = nt;
-    n.pos0 = ti.pos0 + BN;
-    n.kmin = ti.kmin + BN;
-    n.kmax = ti.kmax + BN;
-    n.kp = ti.kp + (int64_t)BN * ti.ss * ELEM;
-    n.vp = ti.vp + (int64_t)BN * ti.ss * ELEM;
+    n.pos0 = ti.pos0 + TB;
+    n.kmin = ti.kmin + TB;
+    n.kmax = ti.kmax + TB;
+    n.kp = ti.kp + (int64_t)TB * ti.ss * ELEM;
+    n.vp = ti.vp + (int64_t)TB * ti.ss * ELEM;
     return n;
   }
-  return next_tile<MODE, ELEM>(p, nt, ti.cursor, end, qmax, b, hk);
+  return next_tile<MODE, ELEM, TB>(p, nt, ti.cursor, end, qmax, b, hk);
 }
 
 // Key and value row addresses and position of tile row r; false past the last key.
-template <int MODE, int ELEM>
+template <int MODE, int ELEM, int TB = BN>
 __device__ __forceinline__ bool row_of(const Params& p, const TileInfo& ti, int r, int b, int hk,
                                        const char*& krow, const char*& vrow, int& pos) {
-  const int64_t j = (int64_t)ti.t * BN + r;
+  const int64_t j = (int64_t)ti.t * TB + r;
   if ((ti.flags & 2) && j >= p.Lk) return false;
   if (ti.flags & 1) {
     krow = ti.kp + (int64_t)r * ti.ss * ELEM;
@@ -643,6 +643,143 @@ __device__ __forceinline__ int wave_mode(const TileInfo& ti, int wqmin, int wqma
   return (ti.flags & 2) ? 2 : 1;
 }
 
+// Work item of a workgroup and the query row of each lane.
+struct Work {
+  int b, hk, hq, split;
+  int64_t qrow_idx;         // (batch, head, row) index of the lane's query row
+  bool valid;               // the lane's row exists
+  int qpos;                 // global position of the lane's query (causal), else kPosAll
+  int wqmin, wqmax, gqmax;  // bounds of the query positions over the wave and the workgroup
+};
+
+template <int MODE>
+__device__ __forceinline__ Work decode_work(const Params& p, int* qred, int wave, int lane) {
+  Work wk;
+  // Blocks are dealt to the 8 XCDs round-robin; remap so that each XCD gets a
+  // contiguous range of work items, and order items so that the blocks sharing
+  // one key/value head and key range (all query tiles of a head, and all query
+  // heads of a GQA group) are adjacent and share that XCD's L2.
+  int w = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) w = (w & 7) * (nwg >> 3) + (w >> 3);
+  const int group = p.Hq / p.Hkv;
+  const int g = w % group;
+  w /= group;
+  int qt = w % p.n_qt;
+  w /= p.n_qt;
+  wk.split = w % p.nsplit;
+  w /= p.nsplit;
+  wk.hk = w % p.Hkv;
+  wk.b = w / p.Hkv;
+  if (MODE == kRingCausal) qt = p.n_qt - 1 - qt;  // later queries see more keys: start them first
+  wk.hq = wk.hk * group + g;
+
+  const int64_t row = (int64_t)qt * BM + wave * 32 + (lane & 31);
+  wk.valid = row < p.Lq;
+  wk.qrow_idx = ((int64_t)wk.b * p.Hq + wk.hq) * p.Lq + (wk.valid ? row : 0);
+
+  wk.qpos = kPosAll;
+  wk.wqmin = kPosAll;
+  wk.wqmax = kPosAll;
+  wk.gqmax = kPosAll;
+  if (MODE == kRingCausal) {
+    wk.qpos = wk.valid ? query_pos(p, row) : kPosMin;
+    wk.wqmin = __builtin_amdgcn_readfirstlane(wave_min(wk.valid ? wk.qpos : kPosNone));
+    wk.wqmax = __builtin_amdgcn_readfirstlane(wave_max(wk.valid ? wk.qpos : kPosMin));
+    if (lane == 0) {
+      qred[wave] = wk.wqmin;
+      qred[kWaves + wave] = wk.wqmax;
+    }
+    __syncthreads();
+    int gq = qred[kWaves];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) gq = max(gq, qred[kWaves + i]);
+    wk.gqmax = __builtin_amdgcn_readfirstlane(gq);
+  }
+  return wk;
+}
+
+// Epilogue: combine the two half-waves' denominators, then write the lane's row
+// (normalised output and lse, chunk statistics, or a key-range partial).
+template <int DP, int MODE>
+__device__ __forceinline__ void write_rows(const Params& p, const Work& wk, f32x16* o, float l_run, float m_ref,
+                                           float m_max, int h) {
+  float l = sum_xor32(l_run);
+  if (MODE == kStats && m_max != m_ref) {
+    // report statistics relative to the true row maximum
+    const float f = __builtin_amdgcn_exp2f((m_ref - m_max) * p.c2);
+    l *= f;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db) o[db] *= f;
+    m_ref = m_max;
+  }
+  if (!wk.valid) return;
+  float* orow;
+  float inv = 1.f;
+  if (p.nsplit > 1) {
+    const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
+    orow = p.part + ((int64_t)wk.split * rows + wk.qrow_idx) * p.d;
+  } else {
+    orow = p.o + wk.qrow_idx * p.d;
+    if (MODE != kStats) inv = (l > 0.f) ? 1.f / l : 0.f;
+  }
+#pragma unroll
+  for (int db = 0; db < DP / 32; ++db) {
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int c0 = db * 32 + 8 * gi + 4 * h;
+      const f32x4 v = {o[db][4 * gi] * inv, o[db][4 * gi + 1] * inv, o[db][4 * gi + 2] * inv,
+                       o[db][4 * gi + 3] * inv};
+      if (c0 + 3 < p.d && (p.d & 3) == 0) {
+        *(f32x4*)(orow + c0) = v;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c0 + i < p.d) orow[c0 + i] = v[i];
+      }
+    }
+  }
+  if (h == 0) {
+    if (p.nsplit > 1) {
+      const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
+      float* pl = p.part + (int64_t)p.nsplit * rows * p.d;
+      pl[(int64_t)wk.split * rows + wk.qrow_idx] = l;
+      pl[((int64_t)p.nsplit + wk.split) * rows + wk.qrow_idx] = m_ref;  // raw units
+    } else {
+      const float m_out = (m_ref == -INFINITY) ? -INFINITY : m_ref * p.scale;
+      if (MODE == kStats) {
+        p.l[wk.qrow_idx] = l;
+        p.m[wk.qrow_idx] = m_out;
+      } else if (p.l != nullptr) {
+        p.l[wk.qrow_idx] = (l > 0.f) ? m_out + logf(l) : -INFINITY;
+      }
+    }
+  }
+}
+
+// Tile walk state with every field forced into scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ TileInfo uniform(TileInfo t) {
+  t.t = __builtin_amdgcn_readfirstlane(t.t);
+  t.cursor = __builtin_amdgcn_readfirstlane(t.cursor);
+  t.flags = __builtin_amdgcn_readfirstlane(t.flags);
+  t.kmin = __builtin_amdgcn_readfirstlane(t.kmin);
+  t.kmax = __builtin_amdgcn_readfirstlane(t.kmax);
+  t.pos0 = __builtin_amdgcn_readfirstlane(t.pos0);
+  t.ss = __builtin_amdgcn_readfirstlane(t.ss);
+  t.cend = __builtin_amdgcn_readfirstlane(t.cend);
+  t.kp = uniform_ptr(t.kp);
+  t.vp = uniform_ptr(t.vp);
+  return t;
+}
+
+// fp32 kernel: one tile per iteration, K and V of the next tile fetched from
+// HBM into registers while the current tile is computed.
 template <class T, int DP, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   using O = Ops<T, DP>;
@@ -655,45 +792,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   const int wave = tid >> 6;
   const int h = lane >> 5;
 
-  // Work decode. Blocks are dealt to the 8 XCDs round-robin; remap so that each
-  // XCD gets a contiguous range of work items, and order items so that the
-  // blocks sharing one key/value head and key range (all query tiles of a head,
-  // and all query heads of a GQA group) are adjacent and share that XCD's L2.
-  int w = blockIdx.x;
-  const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) w = (w & 7) * (nwg >> 3) + (w >> 3);
-  const int group = p.Hq / p.Hkv;
-  const int g = w % group;
-  w /= group;
-  int qt = w % p.n_qt;
-  w /= p.n_qt;
-  const int split = w % p.nsplit;
-  w /= p.nsplit;
-  const int hk = w % p.Hkv;
-  const int b = w / p.Hkv;
-  if (MODE == kRingCausal) qt = p.n_qt - 1 - qt;  // later queries see more keys: start them first
-  const int hq = hk * group + g;
-
-  const int64_t row = (int64_t)qt * BM + wave * 32 + (lane & 31);
-  const bool valid = row < p.Lq;
-  const int64_t qrow_idx = ((int64_t)b * p.Hq + hq) * p.Lq + (valid ? row : 0);
-
-  // Query positions and their bounds per wave and per workgroup.
-  int qpos = kPosAll;
-  int wqmin = kPosAll, wqmax = kPosAll, gqmax = kPosAll;
-  if (MODE == kRingCausal) {
-    qpos = valid ? query_pos(p, row) : kPosMin;
-    wqmin = __builtin_amdgcn_readfirstlane(wave_min(valid ? qpos : kPosNone));
-    wqmax = __builtin_amdgcn_readfirstlane(wave_max(valid ? qpos : kPosMin));
-    if (lane == 0) {
-      qred[wave] = wqmin;
-      qred[kWaves + wave] = wqmax;
-    }
-    __syncthreads();
-    gqmax = qred[kWaves];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) gqmax = max(gqmax, qred[kWaves + i]);
-  }
+  const Work wk = decode_work<MODE>(p, qred, wave, lane);
+  const int b = wk.b, hk = wk.hk, split = wk.split;
+  const bool valid = wk.valid;
+  const int64_t qrow_idx = wk.qrow_idx;
+  const int qpos = wk.qpos, wqmin = wk.wqmin, wqmax = wk.wqmax, gqmax = wk.gqmax;
 
   typename O::QFrag qf;
   O::load_q(p, (const T*)p.q + qrow_idx * p.d, valid, h, qf);
@@ -797,58 +900,438 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
     cur = nxt;
   }
 
-  // Epilogue: combine the two half-waves' denominators, then write.
-  float l = sum_xor32(l_run);
-  if (MODE == kStats && m_max != m_ref) {
-    // report statistics relative to the true row maximum
-    const float f = __builtin_amdgcn_exp2f((m_ref - m_max) * p.c2);
-    l *= f;
-#pragma unroll
-    for (int db = 0; db < DP / 32; ++db) o[db] *= f;
-    m_ref = m_max;
+  write_rows<DP, MODE>(p, wk, o, l_run, m_ref, m_max, h);
+}
+
+// Pipelined bf16 path. K and V tiles are row-major [BN][DP] without padding,
+// the 16-byte pieces of each row permuted by an XOR swizzle (piece c of row r
+// sits at position c ^ swz(r)) so that the MFMA operand reads hit distinct LDS
+// banks.
+//
+// Tiles are copied from HBM straight into LDS (global_load_lds, 16 bytes per
+// lane: the lanes of a wave fill 1 KB of consecutive LDS, and each lane loads
+// the piece that belongs in its slot). Slots that hold no data (rows past the
+// last key, pieces past head_dim) load a valid piece of the same tile instead:
+// such keys are masked and such columns meet zero query columns or are never
+// written out, so any finite value will do.
+//
+// Operand reads: the K operand of S^T = K Q^T is one ds_read_b128 per MFMA;
+// the V^T operand of O^T = V^T P^T is two ds_read_b64_tr_b16 per MFMA, which
+// transpose 4x4 blocks of 16-bit values across each group of 16 lanes (lane i
+// of a group receives element i % 4 of source lanes 4k + i / 4, k = 0..3).
+template <int DP, int TB>
+struct PipeOps {
+  static constexpr int CPR = DP / 8;                // 16-byte pieces per row
+  static constexpr int ROWB = DP * 2;               // bytes per row
+  static constexpr int TILE_B = TB * ROWB;          // bytes of a K or V tile
+  static constexpr int NS = TB * CPR / kThreads;    // 16-byte pieces per thread and tile
+  static constexpr int QF = DP / 16;
+  static_assert(NS * kThreads == TB * CPR, "whole pieces per thread");
+
+  // Swizzle: distinct banks for 16 consecutive rows at one piece (K reads) and
+  // for 4 consecutive rows x 4 consecutive pieces (transposing V reads).
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (DP == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else if constexpr (DP == 64) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else return (r >> 2) & 3;
   }
-  if (!valid) return;
-  float* orow;
-  float inv = 1.f;
-  if (p.nsplit > 1) {
-    const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
-    orow = p.part + ((int64_t)split * rows + qrow_idx) * p.d;
-  } else {
-    orow = p.o + qrow_idx * p.d;
-    if (MODE != kStats) inv = (l > 0.f) ? 1.f / l : 0.f;
+
+  struct QFrag {
+    bf16x8 f[QF];
+  };
+  // Per-lane LDS byte offsets of the MFMA operands, fixed for the whole kernel.
+  struct Lanes {
+    int k[QF];          // K operand of k-step kk (add kb * 32 rows)
+    int v[DP / 32][2];  // V operand of d-block db, half h (add ks * 16 rows)
+  };
+
+  static __device__ __forceinline__ Lanes lanes(int lane) {
+    Lanes L;
+    const int r = lane & 31, hsel = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < QF; ++kk) L.k[kk] = r * ROWB + (((2 * kk + hsel) ^ swz(r)) << 4);
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        // rows: keys 4(g/2) + 8hh + j/4 of the 16-key slice; 4 d values from 32db + 16(g%2) + 4(j%4)
+        const int row = 4 * (g >> 1) + 8 * hh + (j >> 2);
+        const int d0 = 32 * db + 16 * (g & 1) + 4 * (j & 3);
+        L.v[db][hh] = row * ROWB + (((d0 >> 3) ^ swz(row)) << 4) + 2 * (d0 & 7);
+      }
+    return L;
   }
+
+  static __device__ __forceinline__ u32x4 load16(const __bf16* row, int c0, int d, bool vec) {
+    if (vec) {
+      if (c0 < d) return gload16(row + c0);
+      return u32x4{0, 0, 0, 0};
+    }
+    uint32_t w[4];
 #pragma unroll
-  for (int db = 0; db < DP / 32; ++db) {
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = (c0 + 2 * i < d) ? gload_u16(row + c0 + 2 * i) : 0u;
+      uint32_t hi = (c0 + 2 * i + 1 < d) ? gload_u16(row + c0 + 2 * i + 1) : 0u;
+      w[i] = lo | (hi << 16);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+  }
+
+  static __device__ __forceinline__ void load_q(const Params& p, const __bf16* qrow, bool valid, int h,
+                                                QFrag& q) {
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const int c0 = db * 32 + 8 * gi + 4 * h;
-      const f32x4 v = {o[db][4 * gi] * inv, o[db][4 * gi + 1] * inv, o[db][4 * gi + 2] * inv,
-                       o[db][4 * gi + 3] * inv};
-      if (c0 + 3 < p.d && (p.d & 3) == 0) {
-        *(f32x4*)(orow + c0) = v;
-      } else {
+    for (int kk = 0; kk < QF; ++kk) {
+      u32x4 x = valid ? load16(qrow, kk * 16 + h * 8, p.d, p.vec) : u32x4{0, 0, 0, 0};
+      q.f[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // Raw scores <q, k> of the tile, transposed: s[kb][r] is key kb*32 + 8(r/4) + 4h + r%4.
+  static __device__ __forceinline__ void qk(const char* kbuf, const QFrag& q, const Lanes& L, f32x16* s) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (c0 + i < p.d) orow[c0 + i] = v[i];
+    for (int kb = 0; kb < TB / 32; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < QF; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < TB / 32; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(kbuf + L.k[kk] + kb * 32 * ROWB);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.f[kk], s[kb], 0, 0, 0);
       }
     }
   }
-  if (h == 0) {
-    if (p.nsplit > 1) {
-      const int64_t rows = (int64_t)p.B * p.Hq * p.Lq;
-      float* pl = p.part + (int64_t)p.nsplit * rows * p.d;
-      pl[(int64_t)split * rows + qrow_idx] = l;
-      pl[((int64_t)p.nsplit + split) * rows + qrow_idx] = m_ref;  // raw units
+
+  // o[db] += V^T P^T over the tile. P fragment ks holds, for the lane's query,
+  // keys 16ks + {0..3, 8..11} (lanes 0-31) or 16ks + {4..7, 12..15} (lanes
+  // 32-63), the order in which the score blocks hold them; the V^T operand is
+  // read in the same key order.
+  static __device__ __forceinline__ void pv(const char* vbuf, const bf16x8* pf, const Lanes& L, f32x16* o) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+#pragma unroll
+    for (int ks = 0; ks < TB / 16; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vbuf + L.v[db][0] + ks * 16 * ROWB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vbuf + L.v[db][1] + ks * 16 * ROWB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // Slot s = i * kThreads + tid of a tile holds physical piece s % CPR of row
+  // s / CPR. Byte offset, from the tile's first row, of the piece that slot i
+  // of this thread receives in a tile of row stride ss2 bytes.
+  static __device__ __forceinline__ uint32_t piece_offset(int i, int tid, uint32_t ss2) {
+    const int sl = i * kThreads + tid;
+    const int r = sl / CPR, c = (sl % CPR) ^ swz(r);
+    return (uint32_t)r * ss2 + (uint32_t)(c * 16);
+  }
+
+  static __device__ __forceinline__ void copy16(const char* src, char* dst_wave) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst_wave, 16, 0, 0);
+  }
+
+  // Tile in one chunk, no tail, head_dim == DP: uniform base plus 32-bit lane offsets.
+  static __device__ __forceinline__ void copy_fast(const char* base, const uint32_t* off, char* dst, int wave) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) copy16(base + off[i], dst + (i * kThreads + wave * 64) * 16);
+  }
+
+  // Any other tile: each slot's row is looked up chunk by chunk.
+  template <int MODE>
+  static __device__ __forceinline__ void copy_slow(const Params& p, const TileInfo& ti, int b, int hk, int tid,
+                                                   int wave, bool is_v, char* dst) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int sl = i * kThreads + tid;
+      const int r = sl / CPR;
+      int c = (sl % CPR) ^ swz(r);
+      const char *kr, *vr;
+      int pos;
+      if (!row_of<MODE, 2, TB>(p, ti, r, b, hk, kr, vr, pos)) row_of<MODE, 2, TB>(p, ti, 0, b, hk, kr, vr, pos);
+      if (c * 8 >= p.d) c = 0;
+      copy16((is_v ? vr : kr) + c * 16, dst + (i * kThreads + wave * 64) * 16);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// bf16 kernel, software-pipelined inside each wave. Iteration j computes the
+// scores of tile j+1 on the matrix cores while the vector ALUs exponentiate
+// tile j (phase A), then accumulates P(j) V(j) on the matrix cores while the
+// vector ALUs reduce the row maxima of tile j+1 (phase B). A wave's own vector
+// instructions issued between its MFMAs run while the matrix core works,
+// whereas a wave that only issues MFMAs keeps the vector instructions of the
+// other wave on its SIMD waiting; so each wave carries both kinds of work,
+// interleaved by the scheduler directives of schedule_phase().
+//
+// LDS holds a ring of two K buffers and a ring of two V buffers: iteration j
+// reads K(j+1) and V(j) and fills K(j+2) and V(j+1), straight from HBM, into
+// the buffers that iteration j-1 read; one barrier per iteration.
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// s_waitcnt immediate that waits for at most n outstanding vector memory
+// operations and nothing else (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+
+// Instruction order for one phase of NM MFMAs, each fed by NR LDS reads: the
+// reads run kAhead MFMAs ahead of their use, and the vector work (NV ALU and NT
+// transcendental instructions) is spread evenly between the MFMAs.
+constexpr int kAhead = 2;
+template <int NM, int NR, int NV, int NT>
+__device__ __forceinline__ void schedule_phase() {
+  constexpr int va = (NV + NM - 1) / NM, ta = (NT + NM - 1) / NM;
+  __builtin_amdgcn_sched_group_barrier(0x100, NR * kAhead, 0);  // LDS read
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (i + kAhead < NM) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    if (va > 0) __builtin_amdgcn_sched_group_barrier(0x002, va, 0);  // VALU
+    if (ta > 0) __builtin_amdgcn_sched_group_barrier(0x400, ta, 0);  // transcendental
+  }
+}
+
+// Causal masks (and the ragged last tile) use the fact that on this path the
+// keys of a tile have consecutive positions pos0 + key: key `key` is masked for
+// the lane's query when key > min(qpos - pos0, keys in the tile - 1). MASK
+// selects the variant that applies it to every tile; without it no tile needs
+// one (no causal mask and a whole number of tiles).
+template <int DP, int MODE, bool MASK>
+__global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(Params p) {
+  constexpr int TB = 64;  // keys per tile
+  using O = PipeOps<DP, TB>;
+  constexpr int NM = DP * TB / 512;  // MFMAs per phase and wave
+  // Buffers per LDS ring (two workgroups per CU share 160 KB) and tiles copied
+  // ahead of the one being read.
+  constexpr int NB = DP == 128 ? 2 : 4;
+  constexpr int D = NB - 1;
+  // One array per ring slot: copies into one slot and reads of another are
+  // then provably disjoint, and the compiler does not make the reads wait for
+  // the copies (it inserts those waits when it cannot tell them apart).
+  static_assert(NB == 2 || NB == 4, "two or four slots per ring");
+  constexpr int XB = NB == 4 ? O::TILE_B : 16;  // size of slots 2 and 3
+  __shared__ __attribute__((aligned(16))) char k0[O::TILE_B], k1[O::TILE_B], k2[XB], k3[XB];
+  __shared__ __attribute__((aligned(16))) char v0[O::TILE_B], v1[O::TILE_B], v2[XB], v3[XB];
+  char* const kbuf[4] = {k0, k1, k2, k3};
+  char* const vbuf[4] = {v0, v1, v2, v3};
+  __shared__ int qred[2 * kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+
+  const Work wk = decode_work<MODE>(p, qred, wave, lane);
+  const int b = wk.b, hk = wk.hk;
+  const typename O::Lanes L = O::lanes(lane);
+
+  typename O::QFrag qf;
+  O::load_q(p, (const __bf16*)p.q + wk.qrow_idx * p.d, wk.valid, h, qf);
+  // Drain the query loads here, once: otherwise the wait-count analysis carries
+  // them into the tile loop.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  f32x16 o[DP / 32];
+#pragma unroll
+  for (int db = 0; db < DP / 32; ++db) o[db] = f32x16{};
+  float m_ref = -INFINITY;  // reference max (raw dot products <q, k>) that u and l are relative to
+  float m_max = -INFINITY;  // true running max (the chunk-stats call reports it)
+  float l_run = 0.f;        // this lane's share of the running denominator
+  float alpha = 1.f;        // factor taking l and u to the reference of the next tile to exponentiate
+  float ms = 0.f;           // that reference, in exp2 units
+  bool rescale = false;     // some lane of the wave has alpha != 1
+  const float c2 = p.c2;
+
+  const int ntiles = (int)((p.Lk + TB - 1) / TB);
+  const int tbeg = (int)((int64_t)ntiles * wk.split / p.nsplit);
+  const int tend = (int)((int64_t)ntiles * (wk.split + 1) / p.nsplit);
+
+  // Row maximum of a tile's scores (already masked); the reference moves when a
+  // score exceeds it by more than 2^kLazy.
+  // A tile that does not exist (real == false) leaves the state unchanged.
+  auto update_max = [&](const f32x16* s, bool real) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int k2 = 0; k2 < TB / 32; ++k2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mt = fmax_raw(mt, fmax_raw(s[k2][r], s[k2][r + 1]));
+    mt = real ? max_xor32(mt) : -INFINITY;
+    if constexpr (MODE == kStats) m_max = fmax_raw(m_max, mt);
+    const bool need = mt * c2 > m_ref * c2 + kLazy;
+    alpha = need ? __builtin_amdgcn_exp2f((m_ref - mt) * c2) : 1.f;
+    m_ref = need ? mt : m_ref;
+    ms = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
+    rescale = __any(need);
+  };
+
+  // P = exp2(s * c2 - ms) as bf16 fragments; the row sum of the rounded P goes to l.
+  auto exponentiate = [&](const f32x16* s, bf16x8* pf) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float part[TB / 16];
+#pragma unroll
+    for (int ks = 0; ks < TB / 16; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        pf[ks][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + t], c2, -ms));
+      const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // copy the element first: a bit cast of a vector-element lvalue reads element 0
+        const uint32_t wi = w[i];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wi), ones, acc, false);
+      }
+      part[ks] = acc;
+    }
+    float rs = part[0];
+#pragma unroll
+    for (int ks = 1; ks < TB / 16; ++ks) rs += part[ks];
+    l_run = fmaf(l_run, alpha, rs);
+  };
+
+  auto rescale_o = [&]() {
+    if (rescale) {
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db) o[db] *= alpha;
+    }
+  };
+
+  // Keys of tile t (first key at position pos0) that this lane may see: those
+  // with index <= the returned bound (minus 4h, the lane's offset inside each
+  // group of 8 keys).
+  auto key_bound = [&](int t, int pos0) {
+    const int nvalid = (int)min((int64_t)TB, p.Lk - (int64_t)t * TB);
+    const int bound = wk.qpos < pos0 ? -1 : min(wk.qpos - pos0, nvalid - 1);
+    return bound - 4 * h;
+  };
+  auto mask_tile = [&](f32x16* s, int bound) {
+#pragma unroll
+    for (int k2 = 0; k2 < TB / 32; ++k2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k2 * 32 + 8 * (r >> 2) + (r & 3) > bound) s[k2][r] = -INFINITY;
+  };
+
+  uint32_t off[O::NS];
+  int off_ss = -1;
+  auto stage = [&](const TileInfo& t, bool is_v, char* dst) {
+    if (fast_tile(p, t, DP)) {
+      if (t.ss != off_ss) {
+        off_ss = t.ss;
+#pragma unroll
+        for (int i = 0; i < O::NS; ++i) off[i] = O::piece_offset(i, tid, 2u * (uint32_t)t.ss);
+      }
+      O::copy_fast(is_v ? t.vp : t.kp, off, dst, wave);
     } else {
-      const float m_out = (m_ref == -INFINITY) ? -INFINITY : m_ref * p.scale;
-      if (MODE == kStats) {
-        p.l[qrow_idx] = l;
-        p.m[qrow_idx] = m_out;
-      } else if (p.l != nullptr) {
-        p.l[qrow_idx] = (l > 0.f) ? m_out + logf(l) : -INFINITY;
+      O::template copy_slow<MODE>(p, t, b, hk, tid, wave, is_v, dst);
+    }
+  };
+
+  // Copies into LDS go out in groups: group i = {K(i+1+D), V(i+D)}, issued at
+  // iteration i (the prologue issues K(0) and the groups i = -D .. -1).
+  // Iteration j needs group j-D; the D-1 groups issued after it may still be
+  // in flight when they are whole, i.e. when tile j+D exists.
+  constexpr int kGroupOps = 2 * O::NS;
+  auto wait_group = [&](bool later_groups_whole) {
+    if (later_groups_whole)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * kGroupOps));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+
+  const TileInfo t0 = uniform(next_tile<MODE, 2, TB>(p, tbeg, 0, tend, wk.gqmax, b, hk));
+  if (t0.t < tend) {
+    f32x16 sa[TB / 32], sb[TB / 32];
+    bf16x8 pf[TB / 16];
+    // Tile index and first position of tiles j .. j+D, in slot (tile mod NB).
+    int qt[NB], qp[NB];
+
+    // Prologue: K(0), then groups {K(k+1), V(k)} for k < D.
+    qt[0] = t0.t;
+    qp[0] = t0.pos0;
+    stage(t0, false, kbuf[0]);
+    TileInfo tv = t0;
+    TileInfo tk = uniform(successor<MODE, 2, TB>(p, t0, tend, wk.gqmax, b, hk));
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      qt[k + 1] = tk.t;
+      qp[k + 1] = tk.pos0;
+      if (tk.t < tend) stage(tk, false, kbuf[k + 1]);
+      if (tv.t < tend) stage(tv, true, vbuf[k]);
+      tv = tk;
+      if (tk.t < tend) tk = uniform(successor<MODE, 2, TB>(p, tk, tend, wk.gqmax, b, hk));
+    }
+    // K(0) has landed once at most the D groups after it are in flight.
+    if (qt[D] < tend)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(D * kGroupOps));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    O::qk(kbuf[0], qf, L, sa);
+    if constexpr (MASK) mask_tile(sa, key_bound(qt[0], qp[0]));
+    update_max(sa, true);
+
+    // Iteration j (BI = j mod NB): scores of tile j in sc, of tile j+1 into sn.
+    // After the last tile the scores of a missing tile j+1 are computed from
+    // stale LDS and ignored: the loop body stays the same for every tile.
+    // The four ring buffers of a step are passed as restrict pointers: the
+    // compiler then knows that the reads of K(j+1) and V(j) do not touch the
+    // buffers being filled, and does not make them wait for those copies.
+    auto step_body = [&](f32x16* sc, f32x16* sn, auto bi_c, char* __restrict__ k_fill, char* __restrict__ v_fill,
+                         const char* __restrict__ k_read, const char* __restrict__ v_read) {
+      constexpr int BI = decltype(bi_c)::value;
+      wait_group(qt[(BI + D) % NB] < tend);  // K(j+1) and V(j) have landed
+      __syncthreads();
+      rescale_o();  // o to the reference of tile j (after P(j-1) V(j-1))
+      qt[BI] = tk.t;
+      qp[BI] = tk.pos0;
+      if (tk.t < tend) stage(tk, false, k_fill);  // K(j+1+D)
+      if (tv.t < tend) stage(tv, true, v_fill);   // V(j+D)
+      const int bound = MASK ? key_bound(qt[(BI + 1) % NB], qp[(BI + 1) % NB]) : 0;
+
+      // Phase A: S(j+1) = K(j+1) Q^T  ||  P(j) = exp(S(j) - m).
+      O::qk(k_read, qf, L, sn);
+      exponentiate(sc, pf);
+      schedule_phase<NM, 1, TB + 4, TB / 2>();
+      __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: both are MFMA + VALU mixes
+
+      // Phase B: O += P(j) V(j)  ||  mask and row maxima of S(j+1).
+      O::pv(v_read, pf, L, o);
+      if constexpr (MASK) mask_tile(sn, bound);
+      update_max(sn, qt[(BI + 1) % NB] < tend);
+      schedule_phase<NM, 2, TB / 4 + 10 + (MASK ? TB : 0), 1>();
+
+      tv = tk;
+      if (tk.t < tend) tk = uniform(successor<MODE, 2, TB>(p, tk, tend, wk.gqmax, b, hk));
+    };
+    auto step = [&](f32x16* sc, f32x16* sn, auto bi_c) {
+      constexpr int BI = decltype(bi_c)::value;
+      step_body(sc, sn, bi_c, kbuf[BI], vbuf[(BI + D) % NB], kbuf[(BI + 1) % NB], vbuf[BI]);
+    };
+
+    while (true) {
+      step(sa, sb, IntC<0>{});
+      if (qt[1 % NB] >= tend) break;
+      step(sb, sa, IntC<1>{});
+      if (qt[2 % NB] >= tend) break;
+      if constexpr (NB == 4) {
+        step(sa, sb, IntC<2>{});
+        if (qt[3] >= tend) break;
+        step(sb, sa, IntC<3>{});
+        if (qt[0] >= tend) break;
       }
     }
   }
+
+  write_rows<DP, MODE>(p, wk, o, l_run, m_ref, m_max, h);
 }
 
 // Merge of the key-range partials of each row, in range order, then u / l.
@@ -996,6 +1479,15 @@ hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DP, int MODE>
+hipError_t launch_pipe(const Params& p, bool mask, int nblocks, hipStream_t s) {
+  if (mask)
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, true>), dim3(nblocks), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, false>), dim3(nblocks), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_mode(int dtype, int dp, const Params& p, int nblocks, hipStream_t s) {
   if (dtype == RA_BF16) {
@@ -1008,10 +1500,44 @@ hipError_t launch_mode(int dtype, int dp, const Params& p, int nblocks, hipStrea
   return launch_t<float, 128, MODE>(p, nblocks, s);
 }
 
-hipError_t launch(int mode, int dtype, int dp, const Params& p, int nblocks, hipStream_t s) {
+template <int MODE>
+hipError_t launch_pipe_mode(int dp, const Params& p, bool mask, int nblocks, hipStream_t s) {
+  if (dp == 32) return launch_pipe<32, MODE>(p, mask, nblocks, s);
+  if (dp == 64) return launch_pipe<64, MODE>(p, mask, nblocks, s);
+  return launch_pipe<128, MODE>(p, mask, nblocks, s);
+}
+
+// pipe: the pipelined bf16 kernel applies (see pipe_ok); mask: it needs the
+// position mask on every tile.
+hipError_t launch(int mode, int dtype, int dp, const Params& p, bool pipe, bool mask, int nblocks, hipStream_t s) {
+  if (pipe) {
+    if (mode == kStats) return launch_pipe_mode<kStats>(dp, p, mask, nblocks, s);
+    if (mode == kRingFull) return launch_pipe_mode<kRingFull>(dp, p, mask, nblocks, s);
+    return launch_pipe_mode<kRingCausal>(dp, p, mask, nblocks, s);
+  }
   if (mode == kStats) return launch_mode<kStats>(dtype, dp, p, nblocks, s);
   if (mode == kRingFull) return launch_mode<kRingFull>(dtype, dp, p, nblocks, s);
   return launch_mode<kRingCausal>(dtype, dp, p, nblocks, s);
+}
+
+// The pipelined bf16 kernel copies whole 16-byte pieces into LDS with 32-bit
+// lane offsets and masks by key index within a tile, so it needs: bf16,
+// head_dim a multiple of 8, 16-byte aligned rows, row offsets inside a tile
+// below 2^31 bytes, and (when causal) consecutive positions across every chunk
+// boundary that falls inside a tile.
+bool pipe_ok(int dtype, int head_dim, bool vec, const ra_kv_chunk* chunks, int n_chunks, bool causal) {
+  if (dtype != RA_BF16 || head_dim % 8 != 0 || !vec) return false;
+  int64_t start = 0;
+  const ra_kv_chunk* prev = nullptr;
+  for (int c = 0; c < n_chunks; ++c) {
+    const ra_kv_chunk& ch = chunks[c];
+    if (ch.len == 0) continue;
+    if ((int64_t)BN * ch.stride_s * 2 >= ((int64_t)1 << 31)) return false;
+    if (causal && prev && start % BN != 0 && ch.global_offset != prev->global_offset + prev->len) return false;
+    start += ch.len;
+    prev = &ch;
+  }
+  return true;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1099,7 +1625,9 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.vec = vec_ok(q, head_dim, head_dim, elem) && chunk_vec_ok(*chunk, head_dim, elem);
   p.scale = scale;
   p.c2 = scale * kLog2e;
-  hipError_t e = launch(kStats, dtype, dp_of(head_dim), p, (int)nblocks, (hipStream_t)stream);
+  const bool pipe = pipe_ok(dtype, head_dim, p.vec, chunk, 1, false);
+  const bool mask = chunk->len % BN != 0;
+  hipError_t e = launch(kStats, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention_chunk_stats launch");
   return RA_OK;
 }
@@ -1227,7 +1755,9 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   p.vec = vec && vec_ok(q, head_dim, head_dim, elem);
   p.scale = scale;
   p.c2 = scale * kLog2e;
-  e = launch(causal ? kRingCausal : kRingFull, dtype, dp_of(head_dim), p, (int)nblocks, hs);
+  const bool pipe = pipe_ok(dtype, head_dim, p.vec, chunks, n_chunks, causal != 0);
+  const bool mask = causal || lk % BN != 0;
+  e = launch(causal ? kRingCausal : kRingFull, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, hs);
   if (e != hipSuccess) return hip_fail(e, "ring_attention launch");
   if (nsplit > 1) {
     int lpr = 1, sh = 0;
