@@ -1162,9 +1162,9 @@ __global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(Params p) {
     for (int k2 = 0; k2 < TB / 32; ++k2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mt = fmax_raw(mt, fmax_raw(s[k2][r], s[k2][r + 1]));
-    mt = real ? max_xor32(mt) : -INFINITY;
-    if constexpr (MODE == kStats) m_max = fmax_raw(m_max, mt);
-    const bool need = mt * c2 > m_ref * c2 + kLazy;
+    mt = max_xor32(mt);
+    if constexpr (MODE == kStats) m_max = real ? fmax_raw(m_max, mt) : m_max;
+    const bool need = real && mt * c2 > m_ref * c2 + kLazy;
     alpha = need ? __builtin_amdgcn_exp2f((m_ref - mt) * c2) : 1.f;
     m_ref = need ? mt : m_ref;
     ms = (m_ref == -INFINITY) ? 0.f : m_ref * c2;
@@ -1285,9 +1285,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(Params p) {
     // The four ring buffers of a step are passed as restrict pointers: the
     // compiler then knows that the reads of K(j+1) and V(j) do not touch the
     // buffers being filled, and does not make them wait for those copies.
-    auto step_body = [&](f32x16* sc, f32x16* sn, auto bi_c, char* __restrict__ k_fill, char* __restrict__ v_fill,
-                         const char* __restrict__ k_read, const char* __restrict__ v_read) {
+    auto step_body = [&](f32x16* sc, f32x16* sn, auto bi_c, auto mask_c, int bound, char* __restrict__ k_fill,
+                         char* __restrict__ v_fill, const char* __restrict__ k_read,
+                         const char* __restrict__ v_read) {
       constexpr int BI = decltype(bi_c)::value;
+      constexpr bool MASKED = decltype(mask_c)::value != 0;
       wait_group(qt[(BI + D) % NB] < tend);  // K(j+1) and V(j) have landed
       __syncthreads();
       rescale_o();  // o to the reference of tile j (after P(j-1) V(j-1))
@@ -1295,26 +1297,31 @@ __global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(Params p) {
       qp[BI] = tk.pos0;
       if (tk.t < tend) stage(tk, false, k_fill);  // K(j+1+D)
       if (tv.t < tend) stage(tv, true, v_fill);   // V(j+D)
-      const int bound = MASK ? key_bound(qt[(BI + 1) % NB], qp[(BI + 1) % NB]) : 0;
 
       // Phase A: S(j+1) = K(j+1) Q^T  ||  P(j) = exp(S(j) - m).
       O::qk(k_read, qf, L, sn);
       exponentiate(sc, pf);
+      asm volatile("" : "+v"(l_run));  // keeps the row sums here, between the MFMAs
       schedule_phase<NM, 1, TB + 4, TB / 2>();
       __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: both are MFMA + VALU mixes
 
       // Phase B: O += P(j) V(j)  ||  mask and row maxima of S(j+1).
       O::pv(v_read, pf, L, o);
-      if constexpr (MASK) mask_tile(sn, bound);
+      // some lane of the wave cannot see every key of tile j+1 (its highest key
+      // index in a lane is TB - 5 + 4h)
+      if (MASKED && __any(bound < TB - 5)) mask_tile(sn, bound);
       update_max(sn, qt[(BI + 1) % NB] < tend);
-      schedule_phase<NM, 2, TB / 4 + 10 + (MASK ? TB : 0), 1>();
+      schedule_phase<NM, 2, TB / 4 + 10, 1>();
 
       tv = tk;
       if (tk.t < tend) tk = uniform(successor<MODE, 2, TB>(p, tk, tend, wk.gqmax, b, hk));
     };
+    // The masked variant runs only when some lane of the wave cannot see every
+    // key of tile j+1 (its highest key index in a lane is TB - 5 + 4h).
     auto step = [&](f32x16* sc, f32x16* sn, auto bi_c) {
       constexpr int BI = decltype(bi_c)::value;
-      step_body(sc, sn, bi_c, kbuf[BI], vbuf[(BI + D) % NB], kbuf[(BI + 1) % NB], vbuf[BI]);
+      const int bound = MASK ? key_bound(qt[(BI + 1) % NB], qp[(BI + 1) % NB]) : 0;
+      step_body(sc, sn, bi_c, IntC<MASK>{}, bound, kbuf[BI], vbuf[(BI + D) % NB], kbuf[(BI + 1) % NB], vbuf[BI]);
     };
 
     while (true) {
