@@ -53,8 +53,14 @@ SIMD_NUM = 256 * 4
 
 
 def source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the kernel source with // comments and blank lines removed, so that comment edits do
+    not detach the committed counter summaries from the code they were taken on."""
+    import re
+
+    with open(KERNEL_SOURCE) as f:
+        lines = [re.sub(r"\s*//.*$", "", ln).rstrip() for ln in f]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def timed(fn, steps, warmup, torch):
@@ -70,9 +76,15 @@ def timed(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps  # ms per call
 
 
-def traffic_for(workload_name):
+def dominant_kernel(w):
+    """Name of the kernel that does a workload's attention: every bf16 workload here (aligned rows,
+    whole 16-byte pieces) runs the pipelined bf16 kernel, fp32 the general one."""
+    return "attention_bf16_kernel" if w.dtype == "bf16" else "attention_kernel"
+
+
+def traffic_for(w):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
-    path = os.path.join(ROOT, "profiles", f"attention_kernel_{workload_name}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{dominant_kernel(w)}_{w.name}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -196,7 +208,7 @@ def summarize_pmc(args):
     w = wl.config(args.config)
     fetch, write, sq = (_counter_rows(d) for d in args.summarize_pmc)
     copy_name = "neg_kernel"
-    attn_name = "attention_kernel"
+    attn_name = dominant_kernel(w)
     f_copy, _ = _per_dispatch(fetch, copy_name, "FETCH_SIZE")
     w_copy, _ = _per_dispatch(write, copy_name, "WRITE_SIZE")
     f_attn, n_attn = _per_dispatch(fetch, attn_name, "FETCH_SIZE")
@@ -243,7 +255,7 @@ def summarize_pmc(args):
         "dispatches_averaged": n_attn,
         "commands": args.command,
     }
-    path = os.path.join(ROOT, "profiles", f"attention_kernel_{w.name}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{attn_name}_{w.name}_hbm_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -284,7 +296,7 @@ def main():
     ms = timed(step, args.steps, args.warmup, torch)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-    traffic = traffic_for(w.name)
+    traffic = traffic_for(w)
     result = {
         "metric": "ring_attention TFLOP/s at 1 GPU (counted 4*d*Hq*allowed pairs) and % of bf16 MFMA peak",
         "value": round(tflops, 2),

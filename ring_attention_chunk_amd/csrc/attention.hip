@@ -11,29 +11,31 @@
 // Mapping onto the chip
 // ---------------------
 //  * One workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//    owns 32 rows. The workgroup walks key tiles of BN = 64 keys in the order
-//    of the concatenated chunk list, so tile boundaries never depend on how the
+//    owns 32 rows. The workgroup walks key tiles of 64 keys in the order of the
+//    concatenated chunk list, so tile boundaries never depend on how the
 //    sequence was split into chunks: the result is bit-identical for any split.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: lane l then holds one query (l % 32) and 16 of
 //    the 32 keys of a block, so the row max and row sum are in-lane reductions
 //    plus one exchange with lane l ^ 32. The probabilities stay in registers
-//    and feed O^T = V^T P^T directly as the B operand (the key order inside a
-//    16-key slice is permuted; V^T is stored in LDS with the same permutation).
-//  * K and V tiles are double-buffered in LDS; the next tile is fetched from
-//    HBM into registers while the current one is computed, so each tile costs
-//    one workgroup barrier. The fetch of a tile that lies in one chunk is
-//    straight-line vector loads; the loads go through global-address-space
-//    pointers so that waiting on LDS never waits on the HBM prefetch.
-//  * With a causal mask, each tile is classified from global positions: tiles
-//    whose first key lies after every query of the workgroup are skipped (and
-//    whole chunks at once), tiles entirely in the past need no mask, the rest
-//    compare positions per element (positions, never local indices).
+//    and feed O^T = V^T P^T directly as the B operand.
+//  * bf16 (attention_bf16_kernel): each wave software-pipelines its own work,
+//    issuing the MFMAs of the next tile's scores between the vector
+//    instructions of the current tile's softmax, and the current tile's P V
+//    between the next tile's row maxima. K and V tiles are copied from HBM
+//    straight into swizzled LDS rings several tiles ahead; V is read transposed
+//    by the LDS itself.
+//  * fp32, and bf16 inputs the pipelined path cannot copy whole 16-byte pieces
+//    of (attention_kernel): one tile per iteration, the next tile fetched from
+//    HBM into registers while the current one is computed, then stored to
+//    double-buffered LDS (V transposed).
+//  * With a causal mask, tiles and whole chunks whose keys lie after every
+//    query of the workgroup are skipped; tiles with a mix of visible and hidden
+//    keys are masked per element (positions, never local indices).
 //  * When (batch x heads x query tiles) is too small to fill the chip, the key
 //    tiles are cut into equal ranges handled by separate workgroups; their
 //    partial (u, l, m) are merged in range order by a second kernel. The cut
 //    depends only on the number of keys, never on the chunk list.
-//  * fp32 inputs take the same path with v_mfma_f32_32x32x2f32.
 //  * The merge of two statistics is a separate bandwidth-bound kernel.
 
 #include <hip/hip_runtime.h>
