@@ -60,6 +60,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;  // query rows per workgroup
+// Pipelined bf16 kernel: waves per workgroup and workgroups per CU (two waves
+// per SIMD). Eight-wave workgroups halve the copies into LDS per flop but were
+// measured slower: their barrier waits cost more than the copies save.
+constexpr int kPipeWaves = 4;
+constexpr int kPipeThreads = 64 * kPipeWaves;
+constexpr int kPipeBM = 32 * kPipeWaves;
+constexpr int kPipeResident = 8 / kPipeWaves;
+// Keys per tile: 128 at head_dim 64 halves the per-tile costs (barrier, copy
+// issue, tile walk) relative to the matrix work; 64 at 128 for registers.
+constexpr int pipe_tile(int dp) { return dp == 64 ? 128 : 64; }
 constexpr int BN = 64;           // keys per tile
 constexpr int kPosNone = 0x7fffffff;      // position of a missing key: after everything
 constexpr int kPosAll = 0x7ffffffe;       // query position that allows every real key
@@ -654,7 +664,7 @@ struct Work {
   int wqmin, wqmax, gqmax;  // bounds of the query positions over the wave and the workgroup
 };
 
-template <int MODE>
+template <int MODE, int W = kWaves>
 __device__ __forceinline__ Work decode_work(const Params& p, int* qred, int wave, int lane) {
   Work wk;
   // Blocks are dealt to the 8 XCDs round-robin; remap so that each XCD gets a
@@ -676,7 +686,7 @@ __device__ __forceinline__ Work decode_work(const Params& p, int* qred, int wave
   if (MODE == kRingCausal) qt = p.n_qt - 1 - qt;  // later queries see more keys: start them first
   wk.hq = wk.hk * group + g;
 
-  const int64_t row = (int64_t)qt * BM + wave * 32 + (lane & 31);
+  const int64_t row = (int64_t)qt * (32 * W) + wave * 32 + (lane & 31);
   wk.valid = row < p.Lq;
   wk.qrow_idx = ((int64_t)wk.b * p.Hq + wk.hq) * p.Lq + (wk.valid ? row : 0);
 
@@ -690,12 +700,12 @@ __device__ __forceinline__ Work decode_work(const Params& p, int* qred, int wave
     wk.wqmax = __builtin_amdgcn_readfirstlane(wave_max(wk.valid ? wk.qpos : kPosMin));
     if (lane == 0) {
       qred[wave] = wk.wqmin;
-      qred[kWaves + wave] = wk.wqmax;
+      qred[W + wave] = wk.wqmax;
     }
     __syncthreads();
-    int gq = qred[kWaves];
+    int gq = qred[W];
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) gq = max(gq, qred[kWaves + i]);
+    for (int i = 1; i < W; ++i) gq = max(gq, qred[W + i]);
     wk.gqmax = __builtin_amdgcn_readfirstlane(gq);
   }
   return wk;
@@ -921,14 +931,14 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
 // the V^T operand of O^T = V^T P^T is two ds_read_b64_tr_b16 per MFMA, which
 // transpose 4x4 blocks of 16-bit values across each group of 16 lanes (lane i
 // of a group receives element i % 4 of source lanes 4k + i / 4, k = 0..3).
-template <int DP, int TB>
+template <int DP, int TB, int NT>
 struct PipeOps {
   static constexpr int CPR = DP / 8;                // 16-byte pieces per row
   static constexpr int ROWB = DP * 2;               // bytes per row
   static constexpr int TILE_B = TB * ROWB;          // bytes of a K or V tile
-  static constexpr int NS = TB * CPR / kThreads;    // 16-byte pieces per thread and tile
+  static constexpr int NS = TB * CPR / NT;    // 16-byte pieces per thread and tile
   static constexpr int QF = DP / 16;
-  static_assert(NS * kThreads == TB * CPR, "whole pieces per thread");
+  static_assert(NS * NT == TB * CPR, "whole pieces per thread");
 
   // Swizzle: distinct banks for 16 consecutive rows at one piece (K reads) and
   // for 4 consecutive rows x 4 consecutive pieces (transposing V reads).
@@ -1022,11 +1032,11 @@ struct PipeOps {
     }
   }
 
-  // Slot s = i * kThreads + tid of a tile holds physical piece s % CPR of row
+  // Slot s = i * NT + tid of a tile holds physical piece s % CPR of row
   // s / CPR. Byte offset, from the tile's first row, of the piece that slot i
   // of this thread receives in a tile of row stride ss2 bytes.
   static __device__ __forceinline__ uint32_t piece_offset(int i, int tid, uint32_t ss2) {
-    const int sl = i * kThreads + tid;
+    const int sl = i * NT + tid;
     const int r = sl / CPR, c = (sl % CPR) ^ swz(r);
     return (uint32_t)r * ss2 + (uint32_t)(c * 16);
   }
@@ -1039,7 +1049,7 @@ struct PipeOps {
   // Tile in one chunk, no tail, head_dim == DP: uniform base plus 32-bit lane offsets.
   static __device__ __forceinline__ void copy_fast(const char* base, const uint32_t* off, char* dst, int wave) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) copy16(base + off[i], dst + (i * kThreads + wave * 64) * 16);
+    for (int i = 0; i < NS; ++i) copy16(base + off[i], dst + (i * NT + wave * 64) * 16);
   }
 
   // Any other tile: each slot's row is looked up chunk by chunk.
@@ -1048,14 +1058,14 @@ struct PipeOps {
                                                    int wave, bool is_v, char* dst) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int sl = i * kThreads + tid;
+      const int sl = i * NT + tid;
       const int r = sl / CPR;
       int c = (sl % CPR) ^ swz(r);
       const char *kr, *vr;
       int pos;
       if (!row_of<MODE, 2, TB>(p, ti, r, b, hk, kr, vr, pos)) row_of<MODE, 2, TB>(p, ti, 0, b, hk, kr, vr, pos);
       if (c * 8 >= p.d) c = 0;
-      copy16((is_v ? vr : kr) + c * 16, dst + (i * kThreads + wave * 64) * 16);
+      copy16((is_v ? vr : kr) + c * 16, dst + (i * NT + wave * 64) * 16);
     }
   }
 };
@@ -1106,13 +1116,14 @@ __device__ __forceinline__ void schedule_phase() {
 // selects the variant that applies it to every tile; without it no tile needs
 // one (no causal mask and a whole number of tiles).
 template <int DP, int MODE, bool MASK>
-__global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(Params p) {
-  constexpr int TB = 64;  // keys per tile
-  using O = PipeOps<DP, TB>;
+__global__ __launch_bounds__(kPipeThreads, kPipeResident) void attention_bf16_kernel(Params p) {
+  constexpr int W = kPipeWaves;
+  constexpr int TB = pipe_tile(DP);
+  using O = PipeOps<DP, TB, kPipeThreads>;
   constexpr int NM = DP * TB / 512;  // MFMAs per phase and wave
-  // Buffers per LDS ring (two workgroups per CU share 160 KB) and tiles copied
-  // ahead of the one being read.
-  constexpr int NB = DP == 128 ? 2 : 4;
+  // Buffers per LDS ring (the resident workgroups of a CU share 160 KB) and
+  // tiles copied ahead of the one being read.
+  constexpr int NB = 2 * O::TILE_B * 4 * kPipeResident <= 160 * 1024 ? 4 : 2;
   constexpr int D = NB - 1;
   // One array per ring slot: copies into one slot and reads of another are
   // then provably disjoint, and the compiler does not make the reads wait for
@@ -1123,14 +1134,14 @@ __global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char v0[O::TILE_B], v1[O::TILE_B], v2[XB], v3[XB];
   char* const kbuf[4] = {k0, k1, k2, k3};
   char* const vbuf[4] = {v0, v1, v2, v3};
-  __shared__ int qred[2 * kWaves];
+  __shared__ int qred[2 * W];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
 
-  const Work wk = decode_work<MODE>(p, qred, wave, lane);
+  const Work wk = decode_work<MODE, W>(p, qred, wave, lane);
   const int b = wk.b, hk = wk.hk;
   const typename O::Lanes L = O::lanes(lane);
 
@@ -1471,9 +1482,10 @@ int dp_of(int head_dim) { return head_dim <= 32 ? 32 : (head_dim <= 64 ? 64 : 12
 // Key-range split for grids that cannot fill the chip: depends only on the
 // shape (never on the chunk list), so every split of a sequence into chunks
 // runs the same arithmetic.
-int choose_nsplit(int64_t base_blocks, int64_t lk) {
+// `resident`: workgroups of the kernel that fit on one CU at a time.
+int choose_nsplit(int64_t base_blocks, int64_t lk, int resident) {
   const int64_t ntiles = (lk + BN - 1) / BN;
-  const int64_t target = 1024;  // 256 CUs x 2 resident workgroups x 2 rounds
+  const int64_t target = 256 * resident * 2;  // 256 CUs x resident workgroups x 2 rounds
   if (base_blocks >= target / 2) return 1;
   int64_t s = (target + base_blocks - 1) / base_blocks;
   const int64_t max_by_work = ntiles / 16;  // keep at least 16 tiles per range
@@ -1491,9 +1503,9 @@ hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
 template <int DP, int MODE>
 hipError_t launch_pipe(const Params& p, bool mask, int nblocks, hipStream_t s) {
   if (mask)
-    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, true>), dim3(nblocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, true>), dim3(nblocks), dim3(kPipeThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, false>), dim3(nblocks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, false>), dim3(nblocks), dim3(kPipeThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1529,6 +1541,7 @@ hipError_t launch(int mode, int dtype, int dp, const Params& p, bool pipe, bool 
   return launch_mode<kRingCausal>(dtype, dp, p, nblocks, s);
 }
 
+
 // The pipelined bf16 kernel copies whole 16-byte pieces into LDS with 32-bit
 // lane offsets and masks by key index within a tile, so it needs: bf16,
 // head_dim a multiple of 8, 16-byte aligned rows, row offsets inside a tile
@@ -1536,13 +1549,14 @@ hipError_t launch(int mode, int dtype, int dp, const Params& p, bool pipe, bool 
 // boundary that falls inside a tile.
 bool pipe_ok(int dtype, int head_dim, bool vec, const ra_kv_chunk* chunks, int n_chunks, bool causal) {
   if (dtype != RA_BF16 || head_dim % 8 != 0 || !vec) return false;
+  const int tb = pipe_tile(dp_of(head_dim));
   int64_t start = 0;
   const ra_kv_chunk* prev = nullptr;
   for (int c = 0; c < n_chunks; ++c) {
     const ra_kv_chunk& ch = chunks[c];
     if (ch.len == 0) continue;
-    if ((int64_t)BN * ch.stride_s * 2 >= ((int64_t)1 << 31)) return false;
-    if (causal && prev && start % BN != 0 && ch.global_offset != prev->global_offset + prev->len) return false;
+    if ((int64_t)tb * ch.stride_s * 2 >= ((int64_t)1 << 31)) return false;
+    if (causal && prev && start % tb != 0 && ch.global_offset != prev->global_offset + prev->len) return false;
     start += ch.len;
     prev = &ch;
   }
@@ -1584,8 +1598,11 @@ size_t ra_ring_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_l
   if (n_q_segments < 0) n_q_segments = 0;
   size_t bytes = table_bytes(n_chunks, n_q_segments) + 256;
   if (batch > 0 && q_heads > 0 && q_len > 0 && head_dim > 0 && total_keys > 0) {
+    // room for the larger of the two kernels' key-range splits
     const int64_t base = ((q_len + BM - 1) / BM) * (int64_t)q_heads * batch;
-    bytes += partial_bytes(choose_nsplit(base, total_keys), (int64_t)batch * q_heads * q_len, head_dim);
+    const int64_t base_pipe = ((q_len + kPipeBM - 1) / kPipeBM) * (int64_t)q_heads * batch;
+    const int ns = max(choose_nsplit(base, total_keys, 2), choose_nsplit(base_pipe, total_keys, kPipeResident));
+    bytes += partial_bytes(ns, (int64_t)batch * q_heads * q_len, head_dim);
   }
   return bytes;
 }
@@ -1604,7 +1621,9 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   if (q_len == 0 || batch == 0) return RA_OK;
   if (!q || !u || !l || !m) return fail(RA_ERR_NULL, "q, u, l and m must be non-null");
   if (chunk->len > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "chunk longer than 2^31-2 keys");
-  const int64_t n_qt = (q_len + BM - 1) / BM;
+  const bool vec = vec_ok(q, head_dim, head_dim, elem) && chunk_vec_ok(*chunk, head_dim, elem);
+  const bool pipe = pipe_ok(dtype, head_dim, vec, chunk, 1, false);
+  const int64_t n_qt = (q_len + (pipe ? kPipeBM : BM) - 1) / (pipe ? kPipeBM : BM);
   const int64_t nblocks = n_qt * q_heads * batch;
   if (nblocks > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
 
@@ -1631,11 +1650,10 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.d = head_dim;
   p.n_qt = (int)n_qt;
   p.nsplit = 1;
-  p.vec = vec_ok(q, head_dim, head_dim, elem) && chunk_vec_ok(*chunk, head_dim, elem);
+  p.vec = vec;
   p.scale = scale;
   p.c2 = scale * kLog2e;
-  const bool pipe = pipe_ok(dtype, head_dim, p.vec, chunk, 1, false);
-  const bool mask = chunk->len % BN != 0;
+  const bool mask = chunk->len % pipe_tile(dp_of(head_dim)) != 0;
   hipError_t e = launch(kStats, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention_chunk_stats launch");
   return RA_OK;
@@ -1699,9 +1717,12 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   if (lk > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "more than 2^31-2 keys in total");
   if (lq == 0 || batch == 0) return RA_OK;
   if (!q || !out) return fail(RA_ERR_NULL, "q and out must be non-null");
-  const int64_t n_qt = (lq + BM - 1) / BM;
+  const bool pipe = pipe_ok(dtype, head_dim, vec && vec_ok(q, head_dim, head_dim, elem), chunks, n_chunks,
+                            causal != 0);
+  const int bm = pipe ? kPipeBM : BM;
+  const int64_t n_qt = (lq + bm - 1) / bm;
   const int64_t base_blocks = n_qt * q_heads * batch;
-  const int nsplit = lk > 0 ? choose_nsplit(base_blocks, lk) : 1;
+  const int nsplit = lk > 0 ? choose_nsplit(base_blocks, lk, pipe ? kPipeResident : 2) : 1;
   const int64_t nblocks = base_blocks * nsplit;
   if (nblocks > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
   const int64_t rows = (int64_t)batch * q_heads * lq;
@@ -1764,8 +1785,7 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   p.vec = vec && vec_ok(q, head_dim, head_dim, elem);
   p.scale = scale;
   p.c2 = scale * kLog2e;
-  const bool pipe = pipe_ok(dtype, head_dim, p.vec, chunks, n_chunks, causal != 0);
-  const bool mask = causal || lk % BN != 0;
+  const bool mask = causal || lk % pipe_tile(dp_of(head_dim)) != 0;
   e = launch(causal ? kRingCausal : kRingFull, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, hs);
   if (e != hipSuccess) return hip_fail(e, "ring_attention launch");
   if (nsplit > 1) {
