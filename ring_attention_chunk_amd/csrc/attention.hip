@@ -1355,7 +1355,9 @@ __global__ __launch_bounds__(kPipeThreads, kPipeResident) void attention_bf16_ke
 }
 
 // Merge of the key-range partials of each row, in range order, then u / l.
-// Each row is handled by LPR lanes of one wave.
+// Each row is handled by LPR lanes of one wave; with VEC4 (head_dim a multiple
+// of 4) each lane reads and writes 16-byte column groups.
+template <bool VEC4>
 __global__ __launch_bounds__(256) void combine_kernel(int64_t rows, int d, int nsplit, int lpr, int lpr_shift,
                                                       const float* __restrict__ part, float* __restrict__ out,
                                                       float* __restrict__ lse, float c2, float scale) {
@@ -1368,14 +1370,32 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t rows, int d, int n
   for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pm[(int64_t)s * rows + r]);
   const float ms = (mx == -INFINITY) ? 0.f : mx * c2;
   float l = 0.f;
-  for (int s = 0; s < nsplit; ++s)
-    l = fmaf(pl[(int64_t)s * rows + r], __builtin_amdgcn_exp2f(pm[(int64_t)s * rows + r] * c2 - ms), l);
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  for (int c = sub; c < d; c += lpr) {
-    float u = 0.f;
+  if (VEC4) {
+    const int n4 = d >> 2;
+    for (int c = sub; c < n4; c += lpr) {
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+      float lc = 0.f;
+#pragma unroll 4
+      for (int s = 0; s < nsplit; ++s) {
+        const float w = __builtin_amdgcn_exp2f(pm[(int64_t)s * rows + r] * c2 - ms);
+        lc = fmaf(pl[(int64_t)s * rows + r], w, lc);
+        u += ((const f32x4*)(part + ((int64_t)s * rows + r) * d))[c] * w;
+      }
+      l = lc;  // lane 0 of the row always has column group 0
+      const float inv = (lc > 0.f) ? 1.f / lc : 0.f;
+      ((f32x4*)(out + r * d))[c] = u * inv;
+    }
+  } else {
     for (int s = 0; s < nsplit; ++s)
-      u = fmaf(part[((int64_t)s * rows + r) * d + c], __builtin_amdgcn_exp2f(pm[(int64_t)s * rows + r] * c2 - ms), u);
-    out[r * d + c] = u * inv;
+      l = fmaf(pl[(int64_t)s * rows + r], __builtin_amdgcn_exp2f(pm[(int64_t)s * rows + r] * c2 - ms), l);
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    for (int c = sub; c < d; c += lpr) {
+      float u = 0.f;
+      for (int s = 0; s < nsplit; ++s)
+        u = fmaf(part[((int64_t)s * rows + r) * d + c], __builtin_amdgcn_exp2f(pm[(int64_t)s * rows + r] * c2 - ms),
+                 u);
+      out[r * d + c] = u * inv;
+    }
   }
   if (sub == 0 && lse != nullptr) lse[r] = (l > 0.f) ? mx * scale + logf(l) : -INFINITY;
 }
@@ -1482,11 +1502,13 @@ int dp_of(int head_dim) { return head_dim <= 32 ? 32 : (head_dim <= 64 ? 64 : 12
 // Key-range split for grids that cannot fill the chip: depends only on the
 // shape (never on the chunk list), so every split of a sequence into chunks
 // runs the same arithmetic.
-// `resident`: workgroups of the kernel that fit on one CU at a time.
-int choose_nsplit(int64_t base_blocks, int64_t lk, int resident) {
+// `resident`: workgroups of the kernel that fit on one CU at a time; `rounds`:
+// how many times over the grid should fill the chip (2 balances the unequal
+// work of causal query tiles; equal work needs 1).
+int choose_nsplit(int64_t base_blocks, int64_t lk, int resident, int rounds) {
   const int64_t ntiles = (lk + BN - 1) / BN;
-  const int64_t target = 256 * resident * 2;  // 256 CUs x resident workgroups x 2 rounds
-  if (base_blocks >= target / 2) return 1;
+  const int64_t target = 256 * resident * rounds;
+  if (base_blocks >= 256 * resident) return 1;  // one full round already
   int64_t s = (target + base_blocks - 1) / base_blocks;
   const int64_t max_by_work = ntiles / 16;  // keep at least 16 tiles per range
   if (s > max_by_work) s = max_by_work;
@@ -1601,7 +1623,7 @@ size_t ra_ring_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_l
     // room for the larger of the two kernels' key-range splits
     const int64_t base = ((q_len + BM - 1) / BM) * (int64_t)q_heads * batch;
     const int64_t base_pipe = ((q_len + kPipeBM - 1) / kPipeBM) * (int64_t)q_heads * batch;
-    const int ns = max(choose_nsplit(base, total_keys, 2), choose_nsplit(base_pipe, total_keys, kPipeResident));
+    const int ns = max(choose_nsplit(base, total_keys, 2, 2), choose_nsplit(base_pipe, total_keys, kPipeResident, 2));
     bytes += partial_bytes(ns, (int64_t)batch * q_heads * q_len, head_dim);
   }
   return bytes;
@@ -1722,7 +1744,7 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   const int bm = pipe ? kPipeBM : BM;
   const int64_t n_qt = (lq + bm - 1) / bm;
   const int64_t base_blocks = n_qt * q_heads * batch;
-  const int nsplit = lk > 0 ? choose_nsplit(base_blocks, lk, pipe ? kPipeResident : 2) : 1;
+  const int nsplit = lk > 0 ? choose_nsplit(base_blocks, lk, pipe ? kPipeResident : 2, causal ? 2 : 1) : 1;
   const int64_t nblocks = base_blocks * nsplit;
   if (nblocks > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
   const int64_t rows = (int64_t)batch * q_heads * lq;
@@ -1789,14 +1811,20 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   e = launch(causal ? kRingCausal : kRingFull, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, hs);
   if (e != hipSuccess) return hip_fail(e, "ring_attention launch");
   if (nsplit > 1) {
+    const bool vec4 = head_dim % 4 == 0 && (uintptr_t)out % 16 == 0;  // partials are 256-byte aligned
+    const int cols = vec4 ? head_dim / 4 : head_dim;
     int lpr = 1, sh = 0;
-    while (lpr < head_dim && lpr < 64) {
+    while (lpr < cols && lpr < 64) {
       lpr <<= 1;
       ++sh;
     }
     const int64_t cblocks = (rows * lpr + 255) / 256;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)cblocks), dim3(256), 0, hs, rows, head_dim, nsplit, lpr, sh,
-                       (const float*)p.part, out, lse, p.c2, scale);
+    if (vec4)
+      hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)cblocks), dim3(256), 0, hs, rows, head_dim, nsplit,
+                         lpr, sh, (const float*)p.part, out, lse, p.c2, scale);
+    else
+      hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)cblocks), dim3(256), 0, hs, rows, head_dim, nsplit,
+                         lpr, sh, (const float*)p.part, out, lse, p.c2, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "ring_attention combine launch");
   }
