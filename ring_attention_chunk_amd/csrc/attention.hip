@@ -1041,15 +1041,31 @@ struct PipeOps {
     return (uint32_t)r * ss2 + (uint32_t)(c * 16);
   }
 
+  // The copies are issued from inline assembly. The compiler's wait-count
+  // analysis, when it sees LDS written by global_load_lds, waits for every
+  // outstanding LDS read before each use of one (lgkmcnt(0)), which exposes the
+  // LDS latency at every MFMA. Here the copies are invisible to it; the kernel
+  // waits for them itself (vmcnt) before the barrier that publishes a tile.
+  static __device__ __forceinline__ uint32_t lds_addr(char* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) char*)p);
+  }
   static __device__ __forceinline__ void copy16(const char* src, char* dst_wave) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)dst_wave, 16, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_addr(dst_wave))
+                 : "memory", "m0");
+  }
+  static __device__ __forceinline__ void copy16_base(const char* base, uint32_t off, char* dst_wave) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds_addr(dst_wave))
+                 : "memory", "m0");
   }
 
   // Tile in one chunk, no tail, head_dim == DP: uniform base plus 32-bit lane offsets.
   static __device__ __forceinline__ void copy_fast(const char* base, const uint32_t* off, char* dst, int wave) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) copy16(base + off[i], dst + (i * NT + wave * 64) * 16);
+    for (int i = 0; i < NS; ++i) copy16_base(base, off[i], dst + (i * NT + wave * 64) * 16);
   }
 
   // Any other tile: each slot's row is looked up chunk by chunk.
