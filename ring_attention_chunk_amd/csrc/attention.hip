@@ -60,16 +60,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;  // query rows per workgroup
-// Pipelined bf16 kernel: waves per workgroup and workgroups per CU (two waves
-// per SIMD). Eight-wave workgroups halve the copies into LDS per flop but were
-// measured slower: their barrier waits cost more than the copies save.
-constexpr int kPipeWaves = 4;
-constexpr int kPipeThreads = 64 * kPipeWaves;
-constexpr int kPipeBM = 32 * kPipeWaves;
-constexpr int kPipeResident = 8 / kPipeWaves;
-// Keys per tile: 128 at head_dim 64 halves the per-tile costs (barrier, copy
-// issue, tile walk) relative to the matrix work; 64 at 128 for registers.
-constexpr int pipe_tile(int dp) { return dp == 64 ? 128 : 64; }
+// Keys per tile: 128 halves the per-tile costs (barrier, copy issue, tile
+// walk) relative to the matrix work; 64 at head_dim 128 for registers.
+constexpr int pipe_tile(int dp) { return dp == 128 ? 64 : 128; }
 constexpr int BN = 64;           // keys per tile
 constexpr int kPosNone = 0x7fffffff;      // position of a missing key: after everything
 constexpr int kPosAll = 0x7ffffffe;       // query position that allows every real key
@@ -77,6 +70,16 @@ constexpr int kPosMin = -0x7fffffff - 1;  // query position of a missing row
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode { kStats = 0, kRingFull = 1, kRingCausal = 2 };
+
+// Pipelined bf16 kernel: waves per workgroup, by mode; always two waves per
+// SIMD. The ring calls use eight-wave workgroups (256 query rows): one K/V
+// ring per CU instead of two halves the copies into LDS, and the L2 traffic,
+// per flop. The chunk-statistics call keeps four-wave workgroups: it has no
+// key-range split, and 256-row workgroups would leave half the CUs idle on
+// short query shares.
+constexpr int pipe_waves(int mode) { return mode == kStats ? 4 : 8; }
+constexpr int pipe_bm(int mode) { return 32 * pipe_waves(mode); }
+constexpr int pipe_resident(int mode) { return 8 / pipe_waves(mode); }
 
 // Chunk descriptor as the kernels read it (64 bytes).
 struct ChunkDev {
@@ -1013,25 +1016,6 @@ struct PipeOps {
     }
   }
 
-  // o[db] += V^T P^T over the tile. P fragment ks holds, for the lane's query,
-  // keys 16ks + {0..3, 8..11} (lanes 0-31) or 16ks + {4..7, 12..15} (lanes
-  // 32-63), the order in which the score blocks hold them; the V^T operand is
-  // read in the same key order.
-  static __device__ __forceinline__ void pv(const char* vbuf, const bf16x8* pf, const Lanes& L, f32x16* o) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
-#pragma unroll
-    for (int ks = 0; ks < TB / 16; ++ks) {
-#pragma unroll
-      for (int db = 0; db < DP / 32; ++db) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vbuf + L.v[db][0] + ks * 16 * ROWB));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(vbuf + L.v[db][1] + ks * 16 * ROWB));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], o[db], 0, 0, 0);
-      }
-    }
-  }
-
   // Slot s = i * NT + tid of a tile holds physical piece s % CPR of row
   // s / CPR. Byte offset, from the tile's first row, of the piece that slot i
   // of this thread receives in a tile of row stride ss2 bytes.
@@ -1089,16 +1073,16 @@ struct PipeOps {
 // ---------------------------------------------------------------------------
 // bf16 kernel, software-pipelined inside each wave. Iteration j computes the
 // scores of tile j+1 on the matrix cores while the vector ALUs exponentiate
-// tile j (phase A), then accumulates P(j) V(j) on the matrix cores while the
-// vector ALUs reduce the row maxima of tile j+1 (phase B). A wave's own vector
-// instructions issued between its MFMAs run while the matrix core works,
-// whereas a wave that only issues MFMAs keeps the vector instructions of the
-// other wave on its SIMD waiting; so each wave carries both kinds of work,
-// interleaved by the scheduler directives of schedule_phase().
+// tile j and the matrix cores accumulate P(j) V(j): one phase of fixed slots,
+// each holding one score MFMA, one output MFMA and a share of the vector work
+// (see `fused`). A wave's own vector instructions issued between its MFMAs run
+// while the matrix core works; spreading them evenly keeps both busy. The row
+// maximum of tile j+1 is taken in the last slots, from score blocks finished
+// earlier in the phase, so no vector instruction waits on an MFMA in flight.
 //
-// LDS holds a ring of two K buffers and a ring of two V buffers: iteration j
-// reads K(j+1) and V(j) and fills K(j+2) and V(j+1), straight from HBM, into
-// the buffers that iteration j-1 read; one barrier per iteration.
+// LDS holds a ring of NB K buffers and NB V buffers: iteration j reads K(j+1)
+// and V(j) and fills K(j+1+D) and V(j+D), straight from HBM, into buffers read
+// D iterations earlier; one barrier per iteration.
 
 template <int N>
 struct IntC {
@@ -1109,34 +1093,20 @@ struct IntC {
 // operations and nothing else (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
 constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 
-// Instruction order for one phase of NM MFMAs, each fed by NR LDS reads: the
-// reads run kAhead MFMAs ahead of their use, and the vector work (NV ALU and NT
-// transcendental instructions) is spread evenly between the MFMAs.
-constexpr int kAhead = 2;
-template <int NM, int NR, int NV, int NT>
-__device__ __forceinline__ void schedule_phase() {
-  constexpr int va = (NV + NM - 1) / NM, ta = (NT + NM - 1) / NM;
-  __builtin_amdgcn_sched_group_barrier(0x100, NR * kAhead, 0);  // LDS read
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    if (i + kAhead < NM) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-    if (va > 0) __builtin_amdgcn_sched_group_barrier(0x002, va, 0);  // VALU
-    if (ta > 0) __builtin_amdgcn_sched_group_barrier(0x400, ta, 0);  // transcendental
-  }
-}
-
 // Causal masks (and the ragged last tile) use the fact that on this path the
 // keys of a tile have consecutive positions pos0 + key: key `key` is masked for
 // the lane's query when key > min(qpos - pos0, keys in the tile - 1). MASK
 // selects the variant that applies it to every tile; without it no tile needs
 // one (no causal mask and a whole number of tiles).
 template <int DP, int MODE, bool MASK>
-__global__ __launch_bounds__(kPipeThreads, kPipeResident) void attention_bf16_kernel(Params p) {
-  constexpr int W = kPipeWaves;
+__global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void attention_bf16_kernel(Params p) {
+  constexpr int W = pipe_waves(MODE);
+  constexpr int kPipeThreads = 64 * W;
+  constexpr int kPipeResident = pipe_resident(MODE);
   constexpr int TB = pipe_tile(DP);
   using O = PipeOps<DP, TB, kPipeThreads>;
-  constexpr int NM = DP * TB / 512;  // MFMAs per phase and wave
+  constexpr int NM = DP * TB / 512;  // score (and output) MFMAs per tile and wave
+  constexpr int QF_ = O::QF;
   // Buffers per LDS ring (the resident workgroups of a CU share 160 KB) and
   // tiles copied ahead of the one being read.
   constexpr int NB = 2 * O::TILE_B * 4 * kPipeResident <= 160 * 1024 ? 4 : 2;
@@ -1182,15 +1152,19 @@ __global__ __launch_bounds__(kPipeThreads, kPipeResident) void attention_bf16_ke
   const int tbeg = (int)((int64_t)ntiles * wk.split / p.nsplit);
   const int tend = (int)((int64_t)ntiles * (wk.split + 1) / p.nsplit);
 
-  // Row maximum of a tile's scores (already masked); the reference moves when a
-  // score exceeds it by more than 2^kLazy.
+  // Row maximum of a tile's scores (already masked), in two parts: this lane's
+  // share, then the merge over the two lanes of the row and the reference
+  // update. The reference moves when a score exceeds it by more than 2^kLazy.
   // A tile that does not exist (real == false) leaves the state unchanged.
-  auto update_max = [&](const f32x16* s, bool real) {
+  auto lane_max = [&](const f32x16* s) {
     float mt = -INFINITY;
 #pragma unroll
     for (int k2 = 0; k2 < TB / 32; ++k2)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mt = fmax_raw(mt, fmax_raw(s[k2][r], s[k2][r + 1]));
+    return mt;
+  };
+  auto finish_max = [&](float mt, bool real) {
     mt = max_xor32(mt);
     if constexpr (MODE == kStats) m_max = real ? fmax_raw(m_max, mt) : m_max;
     const bool need = real && mt * c2 > m_ref * c2 + kLazy;
@@ -1200,37 +1174,115 @@ __global__ __launch_bounds__(kPipeThreads, kPipeResident) void attention_bf16_ke
     rescale = __any(need);
   };
 
-  // P = exp2(s * c2 - ms) as bf16 fragments; the row sum of the rounded P goes to l.
-  auto exponentiate = [&](const f32x16* s, bf16x8* pf) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float part[TB / 16];
-#pragma unroll
-    for (int ks = 0; ks < TB / 16; ++ks) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        pf[ks][t] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + t], c2, -ms));
-      const u32x4 w = __builtin_bit_cast(u32x4, pf[ks]);
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // copy the element first: a bit cast of a vector-element lvalue reads element 0
-        const uint32_t wi = w[i];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wi), ones, acc, false);
-      }
-      part[ks] = acc;
-    }
-    float rs = part[0];
-#pragma unroll
-    for (int ks = 1; ks < TB / 16; ++ks) rs += part[ks];
-    l_run = fmaf(l_run, alpha, rs);
-  };
-
   auto rescale_o = [&]() {
     if (rescale) {
 #pragma unroll
       for (int db = 0; db < DP / 32; ++db) o[db] *= alpha;
     }
+  };
+
+  // One iteration's matrix work, in NM + NDB slots of fixed content. Slot i
+  // issues score MFMA i of S(j+1) (i < NM) and output MFMA i - NDB of
+  // O += P(j) V(j) (i >= NDB); it exponentiates the share of P(j) that the
+  // output MFMAs of slot i + NDB consume, takes lane maxima of score blocks
+  // that earlier slots finished, and issues the LDS reads of slot i + kRA.
+  // A scheduling barrier closes every slot, so the vector work of a slot runs
+  // under its MFMAs. Score MFMAs go k-step-major over groups of two blocks,
+  // which finishes the first group half way through.
+  constexpr int NBK = TB / 32;         // score blocks of 32 keys
+  constexpr int NDB = DP / 32;         // output blocks of 32 columns
+  constexpr int NSL = NM + NDB;        // slots
+  constexpr int GB = NBK >= 2 ? 2 : 1; // score blocks per group
+  constexpr int NG = NBK / GB;         // groups
+  constexpr int VPS = 8 / NDB;         // P values per slot (8 per 16-key step)
+  constexpr int kRA = 2;               // slots between an LDS read and its use
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  auto fused = [&](const char* __restrict__ k_read, const char* __restrict__ v_read, const f32x16* sc, f32x16* sn,
+                   float& mt_out) {
+    bf16x8 ka[NSL], va[NSL];
+    uint32_t pw[TB / 16][4];
+    auto read_slot = [&](int sl) {
+      if (sl < NM) {
+        const int g = sl / (QF_ * GB), kk = (sl % (QF_ * GB)) / GB, kb = g * GB + sl % GB;
+        ka[sl] = *(const bf16x8*)(k_read + L.k[kk] + kb * 32 * O::ROWB);
+      }
+      const int pi = sl - NDB;
+      if (pi >= 0) {
+        const int ks = pi / NDB, db = pi % NDB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(v_read + L.v[db][0] + ks * 16 * O::ROWB));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(v_read + L.v[db][1] + ks * 16 * O::ROWB));
+        va[sl] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float rs0 = 0.f, rs1 = 0.f;
+    float mx[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) mx[g][0] = mx[g][1] = -INFINITY;
+#pragma unroll
+    for (int sl = 0; sl < kRA; ++sl) read_slot(sl);
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (sl + kRA < NSL) read_slot(sl + kRA);
+      if (sl < NM) {
+        const int g = sl / (QF_ * GB), kk = (sl % (QF_ * GB)) / GB, kb = g * GB + sl % GB;
+        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[sl], qf.f[kk], kk == 0 ? f32x16{} : sn[kb], 0, 0, 0);
+      }
+      if (sl >= NDB) {
+        const int pi = sl - NDB, ks = pi / NDB, db = pi % NDB;
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]});
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[sl], pf, o[db], 0, 0, 0);
+      }
+      if (sl < NM) {
+        // values part*VPS .. part*VPS + VPS - 1 of P step ks
+        const int ks = sl / NDB, part = sl % NDB;
+#pragma unroll
+        for (int w = 0; w < VPS / 2; ++w) {
+          const int t = part * VPS + 2 * w;
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + t], c2, -ms));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + t + 1], c2, -ms));
+          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+          const bf16x2v pr = {(__bf16)x0, (__bf16)x1};
+          const uint32_t word = __builtin_bit_cast(uint32_t, pr);
+          pw[ks][t / 2] = word;
+          if ((t / 2) & 1)
+            rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, rs1, false);
+          else
+            rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, rs0, false);
+        }
+      }
+      // lane maxima: group g finished at slot fin = (g + 1) * QF * GB - 1; its
+      // 16 * GB values per lane are spread over the slots after fin + 1 (the
+      // last group over the remaining slots from fin + 1)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int fin = (g + 1) * QF_ * GB - 1;
+        const int first = (g == NG - 1) ? fin + 1 : fin + 2;
+        const int last = (g == NG - 1) ? NSL - 1 : (g + 2) * QF_ * GB - 1;
+        if (sl >= first && sl <= last) {
+          constexpr int NV = 16 * GB;
+          const int nsl = last - first + 1, k = sl - first;
+          const int v0 = NV * k / nsl, v1 = NV * (k + 1) / nsl;
+#pragma unroll
+          for (int v = v0; v < v1; ++v) {
+            const float x = sn[g * GB + v / 16][v % 16];
+            mx[g][v & 1] = fmax_raw(mx[g][v & 1], x);
+          }
+          asm volatile("" : "+v"(mx[g][0]), "+v"(mx[g][1]));
+        }
+      }
+      // the row sums and maxima have no use inside the phase: without these
+      // empty uses they would all be computed after its last MFMA
+      if (sl < NM) asm volatile("" : "+v"(rs0), "+v"(rs1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = fmaf(l_run, alpha, rs0 + rs1);
+    float mt = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) mt = fmax_raw(mt, fmax_raw(mx[g][0], mx[g][1]));
+    mt_out = mt;
   };
 
   // Keys of tile t (first key at position pos0) that this lane may see: those
@@ -1279,7 +1331,6 @@ __global__ __launch_bounds__(kPipeThreads, kPipeResident) void attention_bf16_ke
   const TileInfo t0 = uniform(next_tile<MODE, 2, TB>(p, tbeg, 0, tend, wk.gqmax, b, hk));
   if (t0.t < tend) {
     f32x16 sa[TB / 32], sb[TB / 32];
-    bf16x8 pf[TB / 16];
     // Tile index and first position of tiles j .. j+D, in slot (tile mod NB).
     int qt[NB], qp[NB];
 
@@ -1306,11 +1357,11 @@ __global__ __launch_bounds__(kPipeThreads, kPipeResident) void attention_bf16_ke
     __syncthreads();
     O::qk(kbuf[0], qf, L, sa);
     if constexpr (MASK) mask_tile(sa, key_bound(qt[0], qp[0]));
-    update_max(sa, true);
+    float mt = lane_max(sa);  // lane maximum of the scores of the next tile to exponentiate
 
     // Iteration j (BI = j mod NB): scores of tile j in sc, of tile j+1 into sn.
     // After the last tile the scores of a missing tile j+1 are computed from
-    // stale LDS and ignored: the loop body stays the same for every tile.
+    // stale LDS and never used: the loop body stays the same for every tile.
     // The four ring buffers of a step are passed as restrict pointers: the
     // compiler then knows that the reads of K(j+1) and V(j) do not touch the
     // buffers being filled, and does not make them wait for those copies.
@@ -1321,32 +1372,24 @@ __global__ __launch_bounds__(kPipeThreads, kPipeResident) void attention_bf16_ke
       constexpr bool MASKED = decltype(mask_c)::value != 0;
       wait_group(qt[(BI + D) % NB] < tend);  // K(j+1) and V(j) have landed
       __syncthreads();
-      rescale_o();  // o to the reference of tile j (after P(j-1) V(j-1))
+      finish_max(mt, true);  // reference for tile j
+      rescale_o();           // o to that reference
       qt[BI] = tk.t;
       qp[BI] = tk.pos0;
       if (tk.t < tend) stage(tk, false, k_fill);  // K(j+1+D)
       if (tv.t < tend) stage(tv, true, v_fill);   // V(j+D)
-
-      // Phase A: S(j+1) = K(j+1) Q^T  ||  P(j) = exp(S(j) - m).
-      O::qk(k_read, qf, L, sn);
-      exponentiate(sc, pf);
-      asm volatile("" : "+v"(l_run));  // keeps the row sums here, between the MFMAs
-      schedule_phase<NM, 1, TB + 4, TB / 2>();
-      __builtin_amdgcn_sched_barrier(0);  // keep the phases apart: both are MFMA + VALU mixes
-
-      // Phase B: O += P(j) V(j)  ||  mask and row maxima of S(j+1).
-      O::pv(v_read, pf, L, o);
+      __builtin_amdgcn_sched_barrier(0);
+      fused(k_read, v_read, sc, sn, mt);
       // some lane of the wave cannot see every key of tile j+1 (its highest key
-      // index in a lane is TB - 5 + 4h)
-      if (MASKED && __any(bound < TB - 5)) mask_tile(sn, bound);
-      update_max(sn, qt[(BI + 1) % NB] < tend);
-      schedule_phase<NM, 2, TB / 4 + 10, 1>();
-
+      // index in a lane is TB - 5 + 4h): mask, and take the maximum again (the
+      // masked maximum never exceeds the one above)
+      if (MASKED && __any(bound < TB - 5)) {
+        mask_tile(sn, bound);
+        mt = fminf(mt, lane_max(sn));
+      }
       tv = tk;
       if (tk.t < tend) tk = uniform(successor<MODE, 2, TB>(p, tk, tend, wk.gqmax, b, hk));
     };
-    // The masked variant runs only when some lane of the wave cannot see every
-    // key of tile j+1 (its highest key index in a lane is TB - 5 + 4h).
     auto step = [&](f32x16* sc, f32x16* sn, auto bi_c) {
       constexpr int BI = decltype(bi_c)::value;
       const int bound = MASK ? key_bound(qt[(BI + 1) % NB], qp[(BI + 1) % NB]) : 0;
@@ -1540,10 +1583,11 @@ hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
 
 template <int DP, int MODE>
 hipError_t launch_pipe(const Params& p, bool mask, int nblocks, hipStream_t s) {
+  constexpr int nt = 64 * pipe_waves(MODE);
   if (mask)
-    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, true>), dim3(nblocks), dim3(kPipeThreads), 0, s, p);
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, true>), dim3(nblocks), dim3(nt), 0, s, p);
   else
-    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, false>), dim3(nblocks), dim3(kPipeThreads), 0, s, p);
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, false>), dim3(nblocks), dim3(nt), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1638,8 +1682,10 @@ size_t ra_ring_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_l
   if (batch > 0 && q_heads > 0 && q_len > 0 && head_dim > 0 && total_keys > 0) {
     // room for the larger of the two kernels' key-range splits
     const int64_t base = ((q_len + BM - 1) / BM) * (int64_t)q_heads * batch;
-    const int64_t base_pipe = ((q_len + kPipeBM - 1) / kPipeBM) * (int64_t)q_heads * batch;
-    const int ns = max(choose_nsplit(base, total_keys, 2, 2), choose_nsplit(base_pipe, total_keys, kPipeResident, 2));
+    const int bmp = pipe_bm(kRingFull);
+    const int64_t base_pipe = ((q_len + bmp - 1) / bmp) * (int64_t)q_heads * batch;
+    const int ns =
+        max(choose_nsplit(base, total_keys, 2, 2), choose_nsplit(base_pipe, total_keys, pipe_resident(kRingFull), 2));
     bytes += partial_bytes(ns, (int64_t)batch * q_heads * q_len, head_dim);
   }
   return bytes;
@@ -1661,7 +1707,8 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   if (chunk->len > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "chunk longer than 2^31-2 keys");
   const bool vec = vec_ok(q, head_dim, head_dim, elem) && chunk_vec_ok(*chunk, head_dim, elem);
   const bool pipe = pipe_ok(dtype, head_dim, vec, chunk, 1, false);
-  const int64_t n_qt = (q_len + (pipe ? kPipeBM : BM) - 1) / (pipe ? kPipeBM : BM);
+  const int bm = pipe ? pipe_bm(kStats) : BM;
+  const int64_t n_qt = (q_len + bm - 1) / bm;
   const int64_t nblocks = n_qt * q_heads * batch;
   if (nblocks > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
 
@@ -1757,10 +1804,10 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   if (!q || !out) return fail(RA_ERR_NULL, "q and out must be non-null");
   const bool pipe = pipe_ok(dtype, head_dim, vec && vec_ok(q, head_dim, head_dim, elem), chunks, n_chunks,
                             causal != 0);
-  const int bm = pipe ? kPipeBM : BM;
+  const int bm = pipe ? pipe_bm(kRingFull) : BM;
   const int64_t n_qt = (lq + bm - 1) / bm;
   const int64_t base_blocks = n_qt * q_heads * batch;
-  const int nsplit = lk > 0 ? choose_nsplit(base_blocks, lk, pipe ? kPipeResident : 2, causal ? 2 : 1) : 1;
+  const int nsplit = lk > 0 ? choose_nsplit(base_blocks, lk, pipe ? pipe_resident(kRingFull) : 2, causal ? 2 : 1) : 1;
   const int64_t nblocks = base_blocks * nsplit;
   if (nblocks > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
   const int64_t rows = (int64_t)batch * q_heads * lq;
