@@ -140,6 +140,20 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
                       void* workspace, size_t workspace_bytes, float* out, float* lse,
                       void* stream);
 
+/* Measurement aid, outside the pages' API: device time of the attention
+ * kernels themselves. While enabled, every ra_ring_attention and
+ * ra_attention_chunk_stats call records a pair of HIP events on its stream,
+ * immediately before and after its attention kernel (the key-range combine
+ * of ra_ring_attention is outside the pair); up to 512 pairs are kept.
+ * ra_kernel_timer(1) creates the events on first use (the only resources the
+ * library ever creates; they live until the process ends), clears the kept
+ * pairs and enables recording; ra_kernel_timer(0) disables it.
+ * ra_kernel_timer_read waits for the kept pairs, writes the sum of their
+ * durations in milliseconds and their number, and clears them. Not
+ * thread-safe; meant for one benchmarking thread. */
+int ra_kernel_timer(int enable);
+int ra_kernel_timer_read(float* total_ms, int* count);
+
 /* Static, human-readable name of a status code. */
 const char* ra_status_string(int status);
 

@@ -27,6 +27,8 @@ EXPORTS = (
     "ra_merge_chunk_stats",
     "ra_ring_workspace_bytes",
     "ra_ring_attention",
+    "ra_kernel_timer",
+    "ra_kernel_timer_read",
     "ra_status_string",
     "ra_last_error",
 )
@@ -76,6 +78,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_ring_attention.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                       ctypes.POINTER(KVChunk), i32, i32, f32, vp, sz, vp, vp, vp]
     lib.ra_ring_attention.restype = i32
+    lib.ra_kernel_timer.argtypes = [i32]
+    lib.ra_kernel_timer.restype = i32
+    lib.ra_kernel_timer_read.argtypes = [ctypes.POINTER(f32), ctypes.POINTER(i32)]
+    lib.ra_kernel_timer_read.restype = i32
     lib.ra_status_string.argtypes = [i32]
     lib.ra_status_string.restype = ctypes.c_char_p
     lib.ra_last_error.argtypes = []
@@ -194,6 +200,21 @@ def merge_chunk_stats(acc, chunk, inplace: bool = False):
 
 
 QOffset = Union[int, Sequence[Tuple[int, int]]]
+
+
+def kernel_timer(enable: bool) -> None:
+    """ra_kernel_timer: start (clearing earlier records) or stop recording the device time of the
+    attention kernel of each call."""
+    lib = load_library()
+    _check(lib, lib.ra_kernel_timer(1 if enable else 0), "kernel_timer")
+
+
+def kernel_timer_read():
+    """ra_kernel_timer_read: (total milliseconds, number of recorded calls), clearing the records."""
+    lib = load_library()
+    tot, n = ctypes.c_float(0.0), ctypes.c_int(0)
+    _check(lib, lib.ra_kernel_timer_read(ctypes.byref(tot), ctypes.byref(n)), "kernel_timer_read")
+    return float(tot.value), int(n.value)
 
 
 def workspace_bytes(query_shape, key_lengths, n_q_segments: int = 1) -> int:

@@ -1691,6 +1691,57 @@ size_t ra_ring_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_l
   return bytes;
 }
 
+// ---------------------------------------------------------------------------
+// Measurement hook: HIP events recorded on the call's stream right before and
+// after the attention kernel of each ring_attention / attention_chunk_stats
+// call (not around the key-range combine), while enabled.
+namespace {
+constexpr int kTimerSlots = 512;
+hipEvent_t g_tev[2][kTimerSlots];
+bool g_tev_made = false;
+int g_timer_on = 0, g_timer_n = 0;
+
+void timer_begin(hipStream_t s) {
+  if (g_timer_on && g_timer_n < kTimerSlots) (void)hipEventRecord(g_tev[0][g_timer_n], s);
+}
+void timer_end(hipStream_t s) {
+  if (g_timer_on && g_timer_n < kTimerSlots) (void)hipEventRecord(g_tev[1][g_timer_n++], s);
+}
+}  // namespace
+
+int ra_kernel_timer(int enable) {
+  g_err[0] = 0;
+  if (enable && !g_tev_made) {
+    for (int i = 0; i < kTimerSlots; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const hipError_t e = hipEventCreate(&g_tev[j][i]);
+        if (e != hipSuccess) return hip_fail(e, "kernel timer: hipEventCreate");
+      }
+    g_tev_made = true;
+  }
+  g_timer_on = enable ? 1 : 0;
+  g_timer_n = 0;
+  return RA_OK;
+}
+
+int ra_kernel_timer_read(float* total_ms, int* count) {
+  g_err[0] = 0;
+  if (!total_ms || !count) return fail(RA_ERR_NULL, "total_ms and count must be non-null");
+  float tot = 0.f;
+  for (int i = 0; i < g_timer_n; ++i) {
+    hipError_t e = hipEventSynchronize(g_tev[1][i]);
+    if (e != hipSuccess) return hip_fail(e, "kernel timer: hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_tev[0][i], g_tev[1][i]);
+    if (e != hipSuccess) return hip_fail(e, "kernel timer: hipEventElapsedTime");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *count = g_timer_n;
+  g_timer_n = 0;
+  return RA_OK;
+}
+
 int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
                              int64_t q_len, const ra_kv_chunk* chunk, float scale, float* u, float* l, float* m,
                              void* stream) {
@@ -1739,7 +1790,9 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.scale = scale;
   p.c2 = scale * kLog2e;
   const bool mask = chunk->len % pipe_tile(dp_of(head_dim)) != 0;
+  timer_begin((hipStream_t)stream);
   hipError_t e = launch(kStats, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, (hipStream_t)stream);
+  timer_end((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention_chunk_stats launch");
   return RA_OK;
 }
@@ -1871,7 +1924,9 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   p.scale = scale;
   p.c2 = scale * kLog2e;
   const bool mask = causal || lk % pipe_tile(dp_of(head_dim)) != 0;
+  timer_begin(hs);
   e = launch(causal ? kRingCausal : kRingFull, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, hs);
+  timer_end(hs);
   if (e != hipSuccess) return hip_fail(e, "ring_attention launch");
   if (nsplit > 1) {
     const bool vec4 = head_dim % 4 == 0 && (uintptr_t)out % 16 == 0;  // partials are 256-byte aligned

@@ -127,3 +127,8 @@ def test_python_layer_refuses_cpu_tensors():
         ra.ring_attention(q, [q], [q])
     with pytest.raises(ra.RingAttentionError):
         ra.attention_chunk_stats(q, q, q)
+
+
+def test_kernel_timer_read_rejects_null(lib):
+    # host-side check only: no event is created or read
+    assert lib.ra_kernel_timer_read(None, None) == 1

@@ -260,6 +260,25 @@ def test_errors_raise():
         ra.ring_attention(q[:, :2], [k], [k], 0, [-5], causal=True)
 
 
+def test_kernel_timer_records_one_pair_per_call():
+    _say("kernel timer")
+    w = wl.custom("timer", "bf16", 1, 2, 2, 64, [(0, 256)], [(0, 512)], False, seed=4)
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    ref = ra.ring_attention(q, kc, vc, 0, [0])
+    torch.cuda.synchronize()
+    ra.api.kernel_timer(True)
+    for _ in range(3):
+        out = ra.ring_attention(q, kc, vc, 0, [0])
+    ra.attention_chunk_stats(q, kc[0], vc[0])
+    total, n = ra.api.kernel_timer_read()
+    ra.api.kernel_timer(False)
+    assert n == 4 and total > 0.0
+    # recording changes nothing in the results
+    assert torch.equal(out, ref)
+    ra.ring_attention(q, kc, vc, 0, [0])
+    assert ra.api.kernel_timer_read() == (0.0, 0)
+
+
 # ---------------------------------------------------------------------------
 # determinism and causal isolation on the GPU
 
