@@ -32,8 +32,10 @@ KERNEL_SOURCE = os.path.join(ROOT, "ring_attention_chunk_amd", "csrc", "attentio
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed calls first (default: as many as take about one second, so that the "
+                         "GPU clocks have settled under load; a cold GPU times several percent slow)")
     ap.add_argument("--config", type=int, default=1, help="workload index (1 is the reported workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,6 +76,17 @@ def timed(fn, steps, warmup, torch):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps  # ms per call
+
+
+def settle_warmup(fn, torch, seconds=1.0, cap=5000):
+    """Number of untimed calls that take about `seconds` (at least 5), from one timed call."""
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    dt = max(time.perf_counter() - t0, 1e-6)
+    return int(min(cap, max(5, round(seconds / dt))))
 
 
 def timed_with_kernel(fn, steps, warmup, torch, api):
@@ -166,6 +179,8 @@ def profile_run(args):
     from ring_attention_chunk_amd import workloads as wl
 
     dev = "cuda:0"
+    if args.warmup is None:
+        args.warmup = 1
     w = wl.config(args.config)
     q, k, v, kc, vc = wl.generate_torch(w, dev)
     offs = [o for o, _ in w.chunks]
@@ -313,6 +328,8 @@ def main():
         return ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, scale=w.softmax_scale,
                                  workspace=ws)
 
+    if args.warmup is None:
+        args.warmup = settle_warmup(step, torch)
     ms, kernel_ms = timed_with_kernel(step, args.steps, args.warmup, torch, ra.api)
     tflops = flops / (ms * 1e-3) / 1e12
     # the roofline is the attention kernel's: its algorithmic flops per launch over its own average
