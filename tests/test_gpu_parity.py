@@ -137,6 +137,12 @@ SMALL = [
     ("bf16_d128_split_causal", "bf16", 1, 2, 1, 128, [(3000, 200)], [(0, 1000), (1000, 2999), (3999, 2001)], True),
     ("bf16_d64_split_nc", "bf16", 2, 2, 2, 64, [(0, 130)], [(0, 4097), (4097, 3000)], False),
     ("f32_d16_split_causal", "f32", 1, 1, 1, 16, [(2500, 40), (100, 40)], [(2000, 2100), (0, 2000)], True),
+    # shapes of the 256-row workgroups and 128-key tiles of the ring kernel: a query share that
+    # ends one row into a workgroup, chunks cut inside a tile, a GQA zigzag at d = 64
+    ("bf16_d32_causal_ragged", "bf16", 1, 2, 2, 32, [(500, 600)], [(0, 700), (700, 77), (777, 400)], True),
+    ("bf16_d64_zigzag_gqa", "bf16", 1, 4, 2, 64, [(128, 128), (896, 128)],
+     [(128 * j, 128) for j in (1, 6, 0, 7, 3, 4, 2, 5)], True),
+    ("bf16_d128_nc_257", "bf16", 1, 2, 2, 128, [(0, 257)], [(0, 300), (300, 211)], False),
 ]
 
 
