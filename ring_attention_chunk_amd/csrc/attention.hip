@@ -1226,31 +1226,54 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
       if (sl + kRA < NSL) read_slot(sl + kRA);
+      // First half of the slot: the score MFMA and the first half of the
+      // exponentials; second half: the output MFMA and the rest. Each MFMA
+      // then has vector work behind it.
+      const int ks = sl / NDB, part = sl % NDB;  // P step and share exponentiated here
+      float xv[VPS];
+      auto expo = [&](int w) {  // exponentials of word w of this slot's share
+        const int t = part * VPS + 2 * w;
+        xv[2 * w] = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + t], c2, -ms));
+        xv[2 * w + 1] = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + t + 1], c2, -ms));
+      };
+      auto pack = [&](int w) {  // bf16 pair and its row sum
+        const int t = part * VPS + 2 * w;
+        typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+        const bf16x2v pr = {(__bf16)xv[2 * w], (__bf16)xv[2 * w + 1]};
+        const uint32_t word = __builtin_bit_cast(uint32_t, pr);
+        pw[ks][t / 2] = word;
+        if ((t / 2) & 1)
+          rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, rs1, false);
+        else
+          rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, rs0, false);
+      };
+      constexpr int WPS = VPS / 2, WA = (WPS + 1) / 2;  // words per slot, words in the first half
       if (sl < NM) {
         const int g = sl / (QF_ * GB), kk = (sl % (QF_ * GB)) / GB, kb = g * GB + sl % GB;
         sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[sl], qf.f[kk], kk == 0 ? f32x16{} : sn[kb], 0, 0, 0);
+#pragma unroll
+        for (int w = 0; w < WA; ++w) expo(w);
+        if (WPS > 1) {
+#pragma unroll
+          for (int w = 0; w < WA; ++w) pack(w);
+          asm volatile("" : "+v"(rs0), "+v"(rs1));
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
       if (sl >= NDB) {
-        const int pi = sl - NDB, ks = pi / NDB, db = pi % NDB;
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]});
+        const int pi = sl - NDB, pks = pi / NDB, db = pi % NDB;
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[pks][0], pw[pks][1], pw[pks][2], pw[pks][3]});
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[sl], pf, o[db], 0, 0, 0);
       }
       if (sl < NM) {
-        // values part*VPS .. part*VPS + VPS - 1 of P step ks
-        const int ks = sl / NDB, part = sl % NDB;
+        if (WPS == 1) {
+          pack(0);
+        } else {
 #pragma unroll
-        for (int w = 0; w < VPS / 2; ++w) {
-          const int t = part * VPS + 2 * w;
-          const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + t], c2, -ms));
-          const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + t + 1], c2, -ms));
-          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-          const bf16x2v pr = {(__bf16)x0, (__bf16)x1};
-          const uint32_t word = __builtin_bit_cast(uint32_t, pr);
-          pw[ks][t / 2] = word;
-          if ((t / 2) & 1)
-            rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, rs1, false);
-          else
-            rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, rs0, false);
+          for (int w = WA; w < WPS; ++w) {
+            expo(w);
+            pack(w);
+          }
         }
       }
       // lane maxima: group g finished at slot fin = (g + 1) * QF * GB - 1; its
