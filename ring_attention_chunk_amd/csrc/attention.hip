@@ -1186,9 +1186,11 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
   // O += P(j) V(j) (i >= NDB); it exponentiates the share of P(j) that the
   // output MFMAs of slot i + NDB consume, takes lane maxima of score blocks
   // that earlier slots finished, and issues the LDS reads of slot i + kRA.
-  // A scheduling barrier closes every slot, so the vector work of a slot runs
-  // under its MFMAs. Score MFMAs go k-step-major over groups of two blocks,
-  // which finishes the first group half way through.
+  // Scheduling barriers split every slot in two, each half one MFMA and part
+  // of the slot's vector work, so the vector work runs under the MFMAs and
+  // neither MFMA waits on the other with nothing behind it. Score MFMAs go
+  // k-step-major over groups of two blocks, which finishes the first group
+  // half way through.
   constexpr int NBK = TB / 32;         // score blocks of 32 keys
   constexpr int NDB = DP / 32;         // output blocks of 32 columns
   constexpr int NSL = NM + NDB;        // slots
