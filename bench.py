@@ -146,14 +146,14 @@ def cpu_baseline(w, q, kc, vc, offs, seconds):
     vh = [c.cpu() for c in vc]
     block = 256
     flops, rows, t0 = 0, 0, time.perf_counter()
-    kpos = np.sort(np.concatenate([np.arange(n) + o for o, n in w.chunks]))
+    kpos = np.sort(wl.k_positions(w))
     h = 0
     r0 = 0
     while time.perf_counter() - t0 < seconds:
         r1 = min(w.lq, r0 + block)
         oracle.attention(qh[:, h:h + 1, r0:r1], [c[:, (h * w.kv_heads) // w.q_heads:][:, :1] for c in kh],
                          [c[:, (h * w.kv_heads) // w.q_heads:][:, :1] for c in vh], qpos[r0:r1], offs,
-                         causal=w.causal, scale=w.softmax_scale)
+                         causal=w.causal, scale=w.softmax_scale, kv_strides=w.kv_strides)
         pairs = (r1 - r0) * w.lk if not w.causal else int(np.searchsorted(kpos, qpos[r0:r1], side="right").sum())
         flops += 4 * w.head_dim * pairs * w.batch
         rows += (r1 - r0) * w.batch
@@ -185,7 +185,8 @@ def profile_run(args):
     q, k, v, kc, vc = wl.generate_torch(w, dev)
     offs = [o for o, _ in w.chunks]
     for _ in range(args.warmup + args.steps):
-        ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, scale=w.softmax_scale)
+        ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
+                          kv_position_strides=w.kv_strides)
     torch.cuda.synchronize()
     del q, k, v, kc, vc
     # calibration: an elementwise kernel that reads COPY_BYTES and writes COPY_BYTES
@@ -325,8 +326,8 @@ def main():
                      dtype=torch.uint8, device=dev)
 
     def step():
-        return ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, scale=w.softmax_scale,
-                                 workspace=ws)
+        return ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
+                                 workspace=ws, kv_position_strides=w.kv_strides)
 
     if args.warmup is None:
         args.warmup = settle_warmup(step, torch)
@@ -360,6 +361,7 @@ def main():
             "keys": w.lk,
             "kv_chunks": len(w.chunks),
             "causal": w.causal,
+            "pos_stride": w.pos_stride,
             "counted_flops": flops,
         },
         "roofline": {

@@ -26,7 +26,7 @@
  *    outputs are fp32.
  *  - head_dim is 1..128; q_heads must be a multiple of kv_heads (query head h
  *    reads key/value head h / (q_heads / kv_heads)).
- *  - Global positions (chunk offsets, query segment offsets, and offset+len)
+ *  - Global positions (every position a chunk or query segment describes)
  *    must lie in [0, 2^31 - 2]; the total number of keys must be < 2^31.
  *
  * Layouts
@@ -63,10 +63,14 @@ enum ra_status {
 
 enum ra_dtype { RA_F32 = 0, RA_BF16 = 1 };
 
-/* One key/value chunk: a contiguous run of global key positions starting at
- * global_offset ("Ring Attention: Distributed Reads with Online Softmax",
- * section "Causal masks depend on global positions": shard metadata carries
- * global positions). Strides are in elements; stride_s >= head_dim. */
+/* One key/value chunk: keys whose global positions form the progression
+ * global_offset + pos_stride * j, j = 0..len-1 ("Ring Attention: Distributed
+ * Reads with Online Softmax", section "Causal masks depend on global
+ * positions": shard metadata carries global positions). pos_stride 1 (or 0,
+ * read as 1) is a contiguous run; pos_stride P is a striped shard, whose keys
+ * are every P-th token of the sequence (glossary "ring attention",
+ * paragraph Variants: striped attention). Memory strides are in elements;
+ * stride_s >= head_dim. */
 typedef struct ra_kv_chunk {
   const void* k;
   const void* v;
@@ -75,13 +79,17 @@ typedef struct ra_kv_chunk {
   int64_t stride_b;
   int64_t stride_h;
   int64_t stride_s;
+  int64_t pos_stride;    /* position step between consecutive keys, >= 0     */
 } ra_kv_chunk;
 
-/* A run of local query rows with consecutive global positions. A contiguous
- * share is one segment; a paired early/late ("zigzag") share is two. */
+/* A run of local query rows whose global positions are global_offset +
+ * pos_stride * i (pos_stride 0 is read as 1). A contiguous share is one
+ * segment with step 1; a paired early/late ("zigzag") share is two; a striped
+ * share is one segment with step P. */
 typedef struct ra_q_segment {
   int64_t len;
   int64_t global_offset;
+  int64_t pos_stride;
 } ra_q_segment;
 
 /* attention_chunk_stats(query, key_chunk, value_chunk) -> (u, l, m).

@@ -44,24 +44,32 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def key_positions(chunk_lengths, kv_offsets) -> np.ndarray:
+def key_positions(chunk_lengths, kv_offsets, kv_strides=None) -> np.ndarray:
     """Global position of every key of the concatenation, in list order.
 
-    A chunk is a contiguous run of positions starting at its global offset
-    (section "Causal masks depend on global positions": shard metadata carries
-    the global positions).
+    Key ``j`` of a chunk sits at ``offset + stride * j`` (section "Causal masks
+    depend on global positions": shard metadata carries the global positions).
+    The stride is 1 for a contiguous shard; a striped shard (glossary "ring
+    attention", paragraph Variants: striped attention) holds every ``P``-th
+    token, stride ``P``.
     """
-    parts = [np.arange(int(n), dtype=np.int64) + int(o) for n, o in zip(chunk_lengths, kv_offsets)]
+    if kv_strides is None:
+        kv_strides = [1] * len(chunk_lengths)
+    parts = [int(o) + int(s) * np.arange(int(n), dtype=np.int64)
+             for n, o, s in zip(chunk_lengths, kv_offsets, kv_strides)]
     return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
 
 
 def query_positions(q_segments) -> np.ndarray:
     """Global position of every local query row.
 
-    ``q_segments`` is a list of ``(global_offset, length)`` runs in row order:
-    one run for a contiguous share, two for a paired early/late share.
+    ``q_segments`` is a list of ``(global_offset, length)`` runs in row order
+    (one run for a contiguous share, two for a paired early/late share), or
+    ``(global_offset, length, stride)`` runs whose positions advance by
+    ``stride`` per row (a striped share).
     """
-    parts = [np.arange(int(n), dtype=np.int64) + int(o) for o, n in q_segments]
+    parts = [int(g[0]) + (int(g[2]) if len(g) > 2 else 1) * np.arange(int(g[1]), dtype=np.int64)
+             for g in q_segments]
     return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
 
 
@@ -95,12 +103,13 @@ def _rows_of_head(q_h, k_h, v_h, qpos, kpos, causal, scale):
 
 
 def attention(q, key_chunks, value_chunks, q_positions=None, kv_offsets=None, causal=False,
-              scale=None, max_block_elems=1 << 24):
+              scale=None, max_block_elems=1 << 24, kv_strides=None):
     """Ordinary attention of every query row against the concatenated chunks.
 
     Returns a dict with ``out`` [B, Hq, Lq, d], ``m``, ``l``, ``lse`` [B, Hq, Lq]
     (fp64). ``q_positions`` [Lq] and ``kv_offsets`` (one per chunk) are global
-    positions; they are required when ``causal`` is true.
+    positions; they are required when ``causal`` is true. ``kv_strides`` (one
+    per chunk, default 1) is each chunk's position step.
     """
     q = _f64(q)
     B, Hq, Lq, d = q.shape
@@ -112,7 +121,7 @@ def attention(q, key_chunks, value_chunks, q_positions=None, kv_offsets=None, ca
         scale = 1.0 / np.sqrt(d)
     if causal:
         qpos = np.asarray(q_positions, dtype=np.int64)
-        kpos = key_positions([c.shape[2] for c in key_chunks], kv_offsets)
+        kpos = key_positions([c.shape[2] for c in key_chunks], kv_offsets, kv_strides)
     else:
         qpos = np.zeros(Lq, dtype=np.int64)
         kpos = np.zeros(k.shape[2], dtype=np.int64)
@@ -134,7 +143,7 @@ def attention(q, key_chunks, value_chunks, q_positions=None, kv_offsets=None, ca
 
 
 def attention_rows(q, key_chunks, value_chunks, rows, q_positions=None, kv_offsets=None,
-                   causal=False, scale=None, max_block_elems=1 << 24):
+                   causal=False, scale=None, max_block_elems=1 << 24, kv_strides=None):
     """The same definition evaluated only on selected ``(b, h, i)`` query rows.
 
     Used where the full output is too large for the CPU (long key sequences):
@@ -149,7 +158,7 @@ def attention_rows(q, key_chunks, value_chunks, rows, q_positions=None, kv_offse
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     lens = [c.shape[2] for c in key_chunks]
-    kpos = key_positions(lens, kv_offsets) if causal else np.zeros(sum(lens), dtype=np.int64)
+    kpos = key_positions(lens, kv_offsets, kv_strides) if causal else np.zeros(sum(lens), dtype=np.int64)
     qpos_all = np.asarray(q_positions, dtype=np.int64) if causal else np.zeros(Lq, dtype=np.int64)
     rows = [tuple(int(x) for x in r) for r in rows]
     R = len(rows)

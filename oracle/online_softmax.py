@@ -86,10 +86,11 @@ def normalize(acc):
 
 
 def ring_attention_fold(q, key_chunks, value_chunks, q_positions=None, kv_offsets=None,
-                        causal=False, scale=None):
+                        causal=False, scale=None, kv_strides=None):
     """Fold the chunks in list order from the identity, then normalise once.
 
-    q [B, Hq, Lq, d]; chunks [B, Hkv, len, d]. Returns ``(out, lse, (u, l, m))``.
+    q [B, Hq, Lq, d]; chunks [B, Hkv, len, d]. ``kv_strides`` (one per chunk,
+    default 1) is each chunk's position step. Returns ``(out, lse, (u, l, m))``.
     """
     q = _f64(q)
     B, Hq, Lq, d = q.shape
@@ -104,7 +105,7 @@ def ring_attention_fold(q, key_chunks, value_chunks, q_positions=None, kv_offset
         vc = np.repeat(vc, group, axis=1)
         allowed = None
         if causal:
-            kpos = key_positions([kc.shape[2]], [kv_offsets[c]])
+            kpos = key_positions([kc.shape[2]], [kv_offsets[c]], None if kv_strides is None else [kv_strides[c]])
             allowed = (kpos[None, :] <= qpos[:, None])[None, None]
         acc = merge_chunk_stats(acc, chunk_stats(q, kc, vc, scale, allowed))
     out, lse = normalize(acc)

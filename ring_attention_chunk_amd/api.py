@@ -43,11 +43,12 @@ class KVChunk(ctypes.Structure):
         ("stride_b", ctypes.c_int64),
         ("stride_h", ctypes.c_int64),
         ("stride_s", ctypes.c_int64),
+        ("pos_stride", ctypes.c_int64),
     ]
 
 
 class QSegment(ctypes.Structure):
-    _fields_ = [("len", ctypes.c_int64), ("global_offset", ctypes.c_int64)]
+    _fields_ = [("len", ctypes.c_int64), ("global_offset", ctypes.c_int64), ("pos_stride", ctypes.c_int64)]
 
 
 class RingAttentionError(RuntimeError):
@@ -123,7 +124,7 @@ def _require_gpu(*ts):
             raise RingAttentionError("tensors must live on the GPU (no CPU path exists)")
 
 
-def _chunk_desc(k, v, offset: int, batch: int, kv_heads: int, head_dim: int) -> KVChunk:
+def _chunk_desc(k, v, offset: int, batch: int, kv_heads: int, head_dim: int, pos_stride: int = 1) -> KVChunk:
     if k.dim() != 4 or v.dim() != 4:
         raise RingAttentionError("key/value chunks must be [batch, kv_heads, len, head_dim]")
     if tuple(k.shape) != tuple(v.shape):
@@ -138,7 +139,8 @@ def _chunk_desc(k, v, offset: int, batch: int, kv_heads: int, head_dim: int) -> 
     sb, sh, ss, _ = k.stride()
     if k.shape[2] <= 1:
         ss = max(ss, head_dim)
-    return KVChunk(k.data_ptr(), v.data_ptr(), int(k.shape[2]), int(offset), int(sb), int(sh), int(ss))
+    return KVChunk(k.data_ptr(), v.data_ptr(), int(k.shape[2]), int(offset), int(sb), int(sh), int(ss),
+                   int(pos_stride))
 
 
 def attention_chunk_stats(query, key_chunk, value_chunk, scale: Optional[float] = None):
@@ -199,7 +201,7 @@ def merge_chunk_stats(acc, chunk, inplace: bool = False):
     return au, al, am
 
 
-QOffset = Union[int, Sequence[Tuple[int, int]]]
+QOffset = Union[int, Sequence[Union[Tuple[int, int], Tuple[int, int, int]]]]
 
 
 def kernel_timer(enable: bool) -> None:
@@ -226,13 +228,17 @@ def workspace_bytes(query_shape, key_lengths, n_q_segments: int = 1) -> int:
 
 def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global_offset: QOffset = 0,
                    kv_global_offsets: Optional[Sequence[int]] = None, causal: bool = False,
-                   scale: Optional[float] = None, return_lse: bool = False, workspace=None):
+                   scale: Optional[float] = None, return_lse: bool = False, workspace=None,
+                   kv_position_strides: Optional[Sequence[int]] = None):
     """Attention of the local queries over all chunks, in list (ring) order, normalised once.
 
     ``q_global_offset`` is the global position of the first query (an int), or
     a list of ``(global_offset, length)`` runs covering the query rows (two
-    runs for a paired early/late share). ``kv_global_offsets`` gives each
-    chunk's first global position; by default chunks follow each other from 0.
+    runs for a paired early/late share), or ``(global_offset, length, step)``
+    runs whose positions advance by ``step`` per row (a striped share).
+    ``kv_global_offsets`` gives each chunk's first global position; by default
+    chunks follow each other from 0. ``kv_position_strides`` gives each
+    chunk's position step (default 1; P for a striped shard of P devices).
     Returns out [B, Hq, Lq, d] fp32 (and lse [B, Hq, Lq] if ``return_lse``).
     """
     torch = _torch()
@@ -254,18 +260,22 @@ def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global
             acc += int(k.shape[2])
     if len(kv_global_offsets) != len(key_chunks):
         raise RingAttentionError("one global offset per chunk is required")
+    if kv_position_strides is None:
+        kv_position_strides = [1] * len(key_chunks)
+    if len(kv_position_strides) != len(key_chunks):
+        raise RingAttentionError("one position stride per chunk is required")
     Hkv = int(key_chunks[0].shape[1]) if key_chunks else Hq
     n = len(key_chunks)
     descs = (KVChunk * max(n, 1))()
-    for i, (k, v, off) in enumerate(zip(key_chunks, value_chunks, kv_global_offsets)):
-        descs[i] = _chunk_desc(k, v, off, B, Hkv, d)
+    for i, (k, v, off, ps) in enumerate(zip(key_chunks, value_chunks, kv_global_offsets, kv_position_strides)):
+        descs[i] = _chunk_desc(k, v, off, B, Hkv, d, ps)
     if isinstance(q_global_offset, int):
-        segs_py = [(int(q_global_offset), Lq)]
+        segs_py = [(int(q_global_offset), Lq, 1)]
     else:
-        segs_py = [(int(o), int(n_)) for o, n_ in q_global_offset]
-    if sum(n_ for _, n_ in segs_py) != Lq:
-        raise RingAttentionError(f"query segments cover {sum(n_ for _, n_ in segs_py)} rows, query has {Lq}")
-    segs = (QSegment * len(segs_py))(*[QSegment(n_, o) for o, n_ in segs_py])
+        segs_py = [(int(g[0]), int(g[1]), int(g[2]) if len(g) > 2 else 1) for g in q_global_offset]
+    if sum(g[1] for g in segs_py) != Lq:
+        raise RingAttentionError(f"query segments cover {sum(g[1] for g in segs_py)} rows, query has {Lq}")
+    segs = (QSegment * len(segs_py))(*[QSegment(n_, o, ps) for o, n_, ps in segs_py])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     total_keys = sum(int(k.shape[2]) for k in key_chunks)

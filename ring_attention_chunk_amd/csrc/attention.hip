@@ -89,13 +89,14 @@ struct ChunkDev {
   int64_t len;
   int64_t sb, sh, ss;
   int32_t pos0;  // global position of the first key
-  int32_t pad;
+  int32_t ps;    // position step between consecutive keys (1: contiguous; P: striped over P devices)
 };
 
 struct QSegDev {
   int64_t row0;
   int64_t len;
   int64_t pos0;
+  int64_t ps;  // position step between consecutive rows
 };
 
 struct Params {
@@ -113,6 +114,7 @@ struct Params {
   int n_qt;
   int nsplit;   // key-tile ranges per (batch, head, query tile)
   int vec;      // 16-byte loads allowed for q, k and v
+  int kps;      // position step shared by every chunk (pipelined causal path only)
   float scale;  // softmax scale
   float c2;     // scale * log2(e)
 };
@@ -169,6 +171,7 @@ struct TileInfo {
   int flags;       // bit 0: all keys from chunk `cursor`; bit 1: the tile runs past the last key
   int kmin, kmax;  // smallest / largest global key position in the tile (causal only)
   int pos0;        // global position of the tile's first row if it lies in one chunk
+  int ps;          // position step between rows of chunk `cursor`
   int ss;          // element stride between rows of chunk `cursor`
   int cend;        // index in the concatenation one past the last key of chunk `cursor`
   const char* kp;  // address of the tile's first key row (batch and head applied)
@@ -196,8 +199,8 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
       while (true) {
         const int64_t lo = max(t0, cc.start), hi = min(t1, cc.start + cc.len);
         if (lo < hi) {
-          kmin = min(kmin, cc.pos0 + (int)(lo - cc.start));
-          kmax = max(kmax, cc.pos0 + (int)(hi - 1 - cc.start));
+          kmin = min(kmin, cc.pos0 + cc.ps * (int)(lo - cc.start));
+          kmax = max(kmax, cc.pos0 + cc.ps * (int)(hi - 1 - cc.start));
         }
         if (c + 1 >= p.n_chunks || cc.start + cc.len >= t1) break;
         ++c;
@@ -220,7 +223,8 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
     ti.flags = (one ? 1 : 0) | ((t0 + TB > p.Lk) ? 2 : 0);
     ti.kmin = kmin;
     ti.kmax = kmax;
-    ti.pos0 = ch.pos0 + (int)(t0 - ch.start);
+    ti.pos0 = ch.pos0 + ch.ps * (int)(t0 - ch.start);
+    ti.ps = ch.ps;
     ti.ss = (int)ch.ss;
     ti.cend = (int)(ch.start + ch.len);
     ti.kp = (const char*)ch.k + off * ELEM;
@@ -233,6 +237,7 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
   ti.kmin = kPosNone;
   ti.kmax = kPosMin;
   ti.pos0 = 0;
+  ti.ps = 1;
   ti.ss = 0;
   ti.cend = 0;
   ti.kp = nullptr;
@@ -247,12 +252,12 @@ __device__ __forceinline__ TileInfo successor(const Params& p, const TileInfo& t
                                               int hk) {
   const int nt = ti.t + 1;
   if (ti.flags == 1 && nt < end && (int64_t)(nt + 1) * TB <= ti.cend &&
-      (MODE != kRingCausal || ti.pos0 + TB <= qmax)) {
+      (MODE != kRingCausal || ti.pos0 + TB * ti.ps <= qmax)) {
     TileInfo n = ti;
     n.t = nt;
-    n.pos0 = ti.pos0 + TB;
-    n.kmin = ti.kmin + TB;
-    n.kmax = ti.kmax + TB;
+    n.pos0 = ti.pos0 + TB * ti.ps;
+    n.kmin = ti.kmin + TB * ti.ps;
+    n.kmax = ti.kmax + TB * ti.ps;
     n.kp = ti.kp + (int64_t)TB * ti.ss * ELEM;
     n.vp = ti.vp + (int64_t)TB * ti.ss * ELEM;
     return n;
@@ -269,7 +274,7 @@ __device__ __forceinline__ bool row_of(const Params& p, const TileInfo& ti, int 
   if (ti.flags & 1) {
     krow = ti.kp + (int64_t)r * ti.ss * ELEM;
     vrow = ti.vp + (int64_t)r * ti.ss * ELEM;
-    pos = ti.pos0 + r;
+    pos = ti.pos0 + r * ti.ps;
     return true;
   }
   int c = ti.cursor;
@@ -281,7 +286,7 @@ __device__ __forceinline__ bool row_of(const Params& p, const TileInfo& ti, int 
   const int64_t off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j - ch.start) * ch.ss;
   krow = (const char*)ch.k + off * ELEM;
   vrow = (const char*)ch.v + off * ELEM;
-  pos = ch.pos0 + (int)(j - ch.start);
+  pos = ch.pos0 + ch.ps * (int)(j - ch.start);
   return true;
 }
 
@@ -423,7 +428,7 @@ struct Ops<__bf16, DP> {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             st.v[i][w] = gload16(ti.vp + ((int64_t)(qd * 4 + w) * ti.ss + cc * 8) * 2);
-            st.pos[i][w] = ti.pos0 + qd * 4 + w;
+            st.pos[i][w] = ti.pos0 + (qd * 4 + w) * ti.ps;
           }
         }
       }
@@ -632,7 +637,7 @@ struct Ops<float, DP> {
 __device__ __forceinline__ int query_pos(const Params& p, int64_t row) {
   for (int s = 0; s < p.n_qseg; ++s) {
     QSegDev g = p.qsegs[s];
-    if (row < g.row0 + g.len) return (int)(g.pos0 + (row - g.row0));
+    if (row < g.row0 + g.len) return (int)(g.pos0 + g.ps * (row - g.row0));
   }
   return kPosMin;
 }
@@ -786,6 +791,7 @@ __device__ __forceinline__ TileInfo uniform(TileInfo t) {
   t.kmin = __builtin_amdgcn_readfirstlane(t.kmin);
   t.kmax = __builtin_amdgcn_readfirstlane(t.kmax);
   t.pos0 = __builtin_amdgcn_readfirstlane(t.pos0);
+  t.ps = __builtin_amdgcn_readfirstlane(t.ps);
   t.ss = __builtin_amdgcn_readfirstlane(t.ss);
   t.cend = __builtin_amdgcn_readfirstlane(t.cend);
   t.kp = uniform_ptr(t.kp);
@@ -1094,8 +1100,9 @@ struct IntC {
 constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 
 // Causal masks (and the ragged last tile) use the fact that on this path the
-// keys of a tile have consecutive positions pos0 + key: key `key` is masked for
-// the lane's query when key > min(qpos - pos0, keys in the tile - 1). MASK
+// keys of a tile have positions pos0 + kps * key in one arithmetic progression
+// (kps = 1 for contiguous shards): key `key` is masked for the lane's query
+// when key > min(floor((qpos - pos0) / kps), keys in the tile - 1). MASK
 // selects the variant that applies it to every tile; without it no tile needs
 // one (no causal mask and a whole number of tiles).
 template <int DP, int MODE, bool MASK>
@@ -1310,13 +1317,15 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
     mt_out = mt;
   };
 
-  // Keys of tile t (first key at position pos0) that this lane may see: those
-  // with index <= the returned bound (minus 4h, the lane's offset inside each
-  // group of 8 keys).
+  // Keys of tile t (first key at position pos0, then every kps positions) that
+  // this lane may see: those with index <= the returned bound (minus 4h, the
+  // lane's offset inside each group of 8 keys). Key i is visible when
+  // pos0 + kps * i <= qpos, i.e. i <= floor((qpos - pos0) / kps).
   auto key_bound = [&](int t, int pos0) {
     const int nvalid = (int)min((int64_t)TB, p.Lk - (int64_t)t * TB);
-    const int bound = wk.qpos < pos0 ? -1 : min(wk.qpos - pos0, nvalid - 1);
-    return bound - 4 * h;
+    int rel = wk.qpos < pos0 ? -1 : wk.qpos - pos0;
+    if (p.kps != 1) rel = rel < 0 ? -1 : rel / p.kps;  // uniform: striped positions only
+    return min(rel, nvalid - 1) - 4 * h;
   };
   auto mask_tile = [&](f32x16* s, int bound) {
 #pragma unroll
@@ -1556,13 +1565,24 @@ int check_dims(int dtype, int batch, int q_heads, int kv_heads, int head_dim) {
   return RA_OK;
 }
 
+// Position step of a chunk or query segment: 0 stands for 1 (contiguous).
+int64_t pos_step(int64_t s) { return s == 0 ? 1 : s; }
+
+// True when offset, offset + step, ..., offset + step * (len - 1) all lie in
+// [0, kPosLimit] (len >= 1, step >= 1).
+bool positions_fit(int64_t offset, int64_t len, int64_t step) {
+  if (offset < 0 || offset > kPosLimit || step < 1 || step > kPosLimit) return false;
+  return len - 1 <= (kPosLimit - offset) / step;
+}
+
 int check_chunk(const ra_kv_chunk& c, int idx, int head_dim) {
   if (c.len < 0) return fail(RA_ERR_SHAPE, "chunk %d: negative length", idx);
+  if (c.pos_stride < 0) return fail(RA_ERR_SHAPE, "chunk %d: negative pos_stride", idx);
   if (c.len == 0) return RA_OK;
   if (!c.k || !c.v) return fail(RA_ERR_NULL, "chunk %d: null k or v", idx);
-  if (c.global_offset < 0 || c.global_offset + c.len - 1 > kPosLimit)
-    return fail(RA_ERR_SHAPE, "chunk %d: positions [%lld, %lld) outside [0, 2^31-1)", idx,
-                (long long)c.global_offset, (long long)(c.global_offset + c.len));
+  if (!positions_fit(c.global_offset, c.len, pos_step(c.pos_stride)))
+    return fail(RA_ERR_SHAPE, "chunk %d: positions %lld + %lld * [0, %lld) outside [0, 2^31-1)", idx,
+                (long long)c.global_offset, (long long)pos_step(c.pos_stride), (long long)c.len);
   if (c.stride_s < head_dim || c.stride_b < 0 || c.stride_h < 0)
     return fail(RA_ERR_SHAPE, "chunk %d: strides b=%lld h=%lld s=%lld invalid for head_dim %d", idx,
                 (long long)c.stride_b, (long long)c.stride_h, (long long)c.stride_s, head_dim);
@@ -1652,21 +1672,29 @@ hipError_t launch(int mode, int dtype, int dp, const Params& p, bool pipe, bool 
 // The pipelined bf16 kernel copies whole 16-byte pieces into LDS with 32-bit
 // lane offsets and masks by key index within a tile, so it needs: bf16,
 // head_dim a multiple of 8, 16-byte aligned rows, row offsets inside a tile
-// below 2^31 bytes, and (when causal) consecutive positions across every chunk
-// boundary that falls inside a tile.
-bool pipe_ok(int dtype, int head_dim, bool vec, const ra_kv_chunk* chunks, int n_chunks, bool causal) {
+// below 2^31 bytes, and (when causal) one position step shared by every chunk
+// (returned in *kps) with positions that continue the progression across
+// every chunk boundary that falls inside a tile.
+bool pipe_ok(int dtype, int head_dim, bool vec, const ra_kv_chunk* chunks, int n_chunks, bool causal, int* kps) {
+  *kps = 1;
   if (dtype != RA_BF16 || head_dim % 8 != 0 || !vec) return false;
   const int tb = pipe_tile(dp_of(head_dim));
-  int64_t start = 0;
+  int64_t start = 0, step = 0;
   const ra_kv_chunk* prev = nullptr;
   for (int c = 0; c < n_chunks; ++c) {
     const ra_kv_chunk& ch = chunks[c];
     if (ch.len == 0) continue;
     if ((int64_t)tb * ch.stride_s * 2 >= ((int64_t)1 << 31)) return false;
-    if (causal && prev && start % tb != 0 && ch.global_offset != prev->global_offset + prev->len) return false;
+    if (causal) {
+      const int64_t s = pos_step(ch.pos_stride);
+      if (step != 0 && s != step) return false;
+      step = s;
+      if (prev && start % tb != 0 && ch.global_offset != prev->global_offset + step * prev->len) return false;
+    }
     start += ch.len;
     prev = &ch;
   }
+  if (step != 0) *kps = (int)step;
   return true;
 }
 
@@ -1782,7 +1810,8 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   if (!q || !u || !l || !m) return fail(RA_ERR_NULL, "q, u, l and m must be non-null");
   if (chunk->len > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "chunk longer than 2^31-2 keys");
   const bool vec = vec_ok(q, head_dim, head_dim, elem) && chunk_vec_ok(*chunk, head_dim, elem);
-  const bool pipe = pipe_ok(dtype, head_dim, vec, chunk, 1, false);
+  int kps = 1;
+  const bool pipe = pipe_ok(dtype, head_dim, vec, chunk, 1, false, &kps);
   const int bm = pipe ? pipe_bm(kStats) : BM;
   const int64_t n_qt = (q_len + bm - 1) / bm;
   const int64_t nblocks = n_qt * q_heads * batch;
@@ -1801,6 +1830,7 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.one.sh = chunk->stride_h;
   p.one.ss = chunk->stride_s;
   p.one.pos0 = 0;
+  p.one.ps = 1;
   p.Lq = q_len;
   p.Lk = chunk->len;
   p.n_chunks = 1;
@@ -1812,6 +1842,7 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.n_qt = (int)n_qt;
   p.nsplit = 1;
   p.vec = vec;
+  p.kps = kps;
   p.scale = scale;
   p.c2 = scale * kLog2e;
   const bool mask = chunk->len % pipe_tile(dp_of(head_dim)) != 0;
@@ -1866,7 +1897,8 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   for (int s = 0; s < n_q_segments; ++s) {
     const ra_q_segment& g = q_segments[s];
     if (g.len < 0) return fail(RA_ERR_SHAPE, "query segment %d: negative length", s);
-    if (causal && g.len > 0 && (g.global_offset < 0 || g.global_offset + g.len - 1 > kPosLimit))
+    if (g.pos_stride < 0) return fail(RA_ERR_SHAPE, "query segment %d: negative pos_stride", s);
+    if (causal && g.len > 0 && !positions_fit(g.global_offset, g.len, pos_step(g.pos_stride)))
       return fail(RA_ERR_SHAPE, "query segment %d: positions outside [0, 2^31-1)", s);
     lq += g.len;
   }
@@ -1880,8 +1912,9 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   if (lk > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "more than 2^31-2 keys in total");
   if (lq == 0 || batch == 0) return RA_OK;
   if (!q || !out) return fail(RA_ERR_NULL, "q and out must be non-null");
+  int kps = 1;
   const bool pipe = pipe_ok(dtype, head_dim, vec && vec_ok(q, head_dim, head_dim, elem), chunks, n_chunks,
-                            causal != 0);
+                            causal != 0, &kps);
   const int bm = pipe ? pipe_bm(kRingFull) : BM;
   const int64_t n_qt = (lq + bm - 1) / bm;
   const int64_t base_blocks = n_qt * q_heads * batch;
@@ -1913,6 +1946,7 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
     d.sh = chunks[c].stride_h;
     d.ss = chunks[c].stride_s;
     d.pos0 = (int32_t)chunks[c].global_offset;
+    d.ps = (int32_t)pos_step(chunks[c].pos_stride);
     start += chunks[c].len;
   }
   int64_t row0 = 0;
@@ -1920,6 +1954,7 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
     hqs[s].row0 = row0;
     hqs[s].len = q_segments[s].len;
     hqs[s].pos0 = q_segments[s].global_offset;
+    hqs[s].ps = pos_step(q_segments[s].pos_stride);
     row0 += q_segments[s].len;
   }
   hipStream_t hs = (hipStream_t)stream;
@@ -1946,6 +1981,7 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   p.n_qt = (int)n_qt;
   p.nsplit = nsplit;
   p.vec = vec && vec_ok(q, head_dim, head_dim, elem);
+  p.kps = kps;
   p.scale = scale;
   p.c2 = scale * kLog2e;
   const bool mask = causal || lk % pipe_tile(dp_of(head_dim)) != 0;

@@ -12,7 +12,11 @@ sequence across devices"); the device at ring index ``r`` meets, at step
 predecessor), so the chunk list below is in that ring order. Section "Causal
 masks depend on global positions" gives the two causal layouts used here:
 contiguous shards and paired early/late chunks ("zigzag": with ``2P`` chunks,
-device ``r`` owns chunks ``r`` and ``2P-1-r``).
+device ``r`` owns chunks ``r`` and ``2P-1-r``). The glossary entry "ring
+attention" (paragraph Variants) adds striped attention, read here as the
+round-robin layout: device ``r`` owns positions ``r, r+P, r+2P, ...``, so a
+shard is a run of positions with step ``P`` (``pos_stride``) and its keys lie
+contiguous in that device's memory.
 
 Values: q, k, v are standard normal fp32, drawn per block of global positions
 from ``numpy.random.default_rng([seed, tensor, block])`` so that any re-split of
@@ -47,6 +51,7 @@ class Workload:
     q_std: float = 1.0
     seed: int = 0
     scale: Optional[float] = None  # None means 1/sqrt(head_dim)
+    pos_stride: int = 1  # position step inside every query run and chunk (P for a striped share)
 
     @property
     def lq(self) -> int:
@@ -59,6 +64,19 @@ class Workload:
     @property
     def softmax_scale(self) -> float:
         return self.scale if self.scale is not None else 1.0 / float(np.sqrt(self.head_dim))
+
+    @property
+    def kv_offsets(self) -> List[int]:
+        return [o for o, _ in self.chunks]
+
+    @property
+    def kv_strides(self) -> List[int]:
+        return [self.pos_stride] * len(self.chunks)
+
+    @property
+    def q_runs(self) -> List[Tuple[int, int, int]]:
+        """Query runs as ``(global_offset, length, position step)``."""
+        return [(o, n, self.pos_stride) for o, n in self.q_segments]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -134,7 +152,19 @@ def long_gqa() -> Workload:
                     [(j * L, L) for j in ring_order(0, P)], False, P * L, q_std=4.0, seed=104)
 
 
-CONFIGS = {0: tiny, 1: noncausal_d64, 2: causal_contiguous, 3: causal_zigzag, 4: long_gqa}
+def causal_striped(P: int = 8, r: int = 5, n: int = 65536, heads: int = 32, d: int = 128) -> Workload:
+    """bf16 striped causal share: device r of P holds positions r, r+P, ...; shard j holds j, j+P, ...
+
+    At the defaults it is the contiguous causal share's shape (32 heads, d=128,
+    n=65536, device 5 of 8) in the striped layout, where every shard is about
+    half visible instead of whole shards being visible or hidden.
+    """
+    L = n // P
+    return Workload(f"causal_striped_r{r}of{P}_h{heads}_d{d}_n{n // 1024}k", "bf16", 1, heads, heads, d,
+                    [(r, L)], [(j, L) for j in ring_order(r, P)], True, n, seed=105, pos_stride=P)
+
+
+CONFIGS = {0: tiny, 1: noncausal_d64, 2: causal_contiguous, 3: causal_zigzag, 4: long_gqa, 5: causal_striped}
 
 
 def config(i: int, **kw) -> Workload:
@@ -142,11 +172,12 @@ def config(i: int, **kw) -> Workload:
 
 
 def custom(name, dtype, batch, q_heads, kv_heads, head_dim, q_segments, chunks, causal,
-           seq_len=None, q_std=1.0, seed=7, scale=None) -> Workload:
+           seq_len=None, q_std=1.0, seed=7, scale=None, pos_stride=1) -> Workload:
     if seq_len is None:
-        seq_len = max([o + n for o, n in chunks] + [o + n for o, n in q_segments] + [0])
+        ends = [o + pos_stride * (n - 1) + 1 for o, n in list(chunks) + list(q_segments) if n > 0]
+        seq_len = max(ends + [0])
     return Workload(name, dtype, batch, q_heads, kv_heads, head_dim, list(q_segments), list(chunks),
-                    causal, seq_len, q_std, seed, scale)
+                    causal, seq_len, q_std, seed, scale, pos_stride)
 
 
 def resplit(w: Workload, cuts: Sequence[int]) -> Workload:
@@ -157,11 +188,12 @@ def resplit(w: Workload, cuts: Sequence[int]) -> Workload:
     at ``cuts``. Every key keeps its place and its global position, so the data
     and the exact result are unchanged.
     """
+    st = w.pos_stride
     runs = []
     for o, n in w.chunks:
         if n == 0:
             continue
-        if runs and runs[-1][0] + runs[-1][1] == o:
+        if runs and runs[-1][0] + st * runs[-1][1] == o:
             runs[-1] = (runs[-1][0], runs[-1][1] + n)
         else:
             runs.append((o, n))
@@ -170,7 +202,7 @@ def resplit(w: Workload, cuts: Sequence[int]) -> Workload:
     for o, n in runs:
         inner = [c - s0 for c in bounds if s0 < c < s0 + n]
         edges = [0] + inner + [n]
-        out += [(o + a, b - a) for a, b in zip(edges[:-1], edges[1:])]
+        out += [(o + st * a, b - a) for a, b in zip(edges[:-1], edges[1:])]
         s0 += n
     return dataclasses.replace(w, chunks=out, name=w.name + "_resplit")
 
@@ -200,8 +232,10 @@ def generate_numpy(w: Workload):
     is ``k[:, :, o:o+len]`` with ``(o, len) = w.chunks[c]``.
     """
     B, Hq, Hkv, d = w.batch, w.q_heads, w.kv_heads, w.head_dim
-    q = np.concatenate([_normal_positions(w.seed, 0, (B, Hq), o, o + n, d) for o, n in w.q_segments],
-                       axis=2) if w.q_segments else np.zeros((B, Hq, 0, d), np.float32)
+    st = w.pos_stride
+    q = np.concatenate([_normal_positions(w.seed, 0, (B, Hq), o, o + st * (n - 1) + 1, d)[..., ::st, :]
+                        for o, n in w.q_segments if n > 0],
+                       axis=2) if any(n > 0 for _, n in w.q_segments) else np.zeros((B, Hq, 0, d), np.float32)
     if w.q_std != 1.0:
         q = q * np.float32(w.q_std)
     k = _normal_positions(w.seed, 1, (B, Hkv), 0, w.seq_len, d)
@@ -216,17 +250,38 @@ def generate_torch(w: Workload, device="cpu"):
 
     Returns ``(q, k_full, v_full, key_chunks, value_chunks)``; the chunk lists
     are views into ``k_full``/``v_full`` in ring order, so no data is copied.
+    With contiguous positions ``k_full`` is in global-position order. A striped
+    share (``pos_stride`` P) keeps each chunk's keys contiguous, as the device
+    owning that shard holds them: ``k_full`` is then the chunks' keys one
+    after another in list order.
     """
     import torch
 
     q, k, v = generate_numpy(w)
+    st = w.pos_stride
+    if st != 1:
+        k = np.concatenate([k[:, :, o:o + st * (n - 1) + 1:st] for o, n in w.chunks if n > 0], axis=2)
+        v = np.concatenate([v[:, :, o:o + st * (n - 1) + 1:st] for o, n in w.chunks if n > 0], axis=2)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     tq = torch.from_numpy(q).to(device=device).to(tdt)
-    tk = torch.from_numpy(k).to(device=device).to(tdt)
-    tv = torch.from_numpy(v).to(device=device).to(tdt)
-    kc = [tk[:, :, o:o + n] for o, n in w.chunks]
-    vc = [tv[:, :, o:o + n] for o, n in w.chunks]
+    tk = torch.from_numpy(np.ascontiguousarray(k)).to(device=device).to(tdt)
+    tv = torch.from_numpy(np.ascontiguousarray(v)).to(device=device).to(tdt)
+    kc, vc = chunk_views(w, tk, tv)
     return tq, tk, tv, kc, vc
+
+
+def chunk_views(w: Workload, k_full, v_full):
+    """Views of ``w``'s chunks in buffers laid out as :func:`generate_torch` lays them out.
+
+    Also valid for any :func:`resplit` of the workload the buffers were made
+    for: contiguous shares are indexed by position, striped ones by the key's
+    place in the concatenated list (which a re-split keeps).
+    """
+    if w.pos_stride == 1:
+        return [k_full[:, :, o:o + n] for o, n in w.chunks], [v_full[:, :, o:o + n] for o, n in w.chunks]
+    starts = np.cumsum([0] + [n for _, n in w.chunks])
+    return ([k_full[:, :, int(a):int(a) + n] for a, (_, n) in zip(starts, w.chunks)],
+            [v_full[:, :, int(a):int(a) + n] for a, (_, n) in zip(starts, w.chunks)])
 
 
 # ---------------------------------------------------------------------------
@@ -234,7 +289,13 @@ def generate_torch(w: Workload, device="cpu"):
 
 
 def q_positions(w: Workload) -> np.ndarray:
-    parts = [np.arange(n, dtype=np.int64) + o for o, n in w.q_segments]
+    parts = [o + w.pos_stride * np.arange(n, dtype=np.int64) for o, n in w.q_segments]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
+def k_positions(w: Workload) -> np.ndarray:
+    """Global position of every key, in list (ring) order."""
+    parts = [o + w.pos_stride * np.arange(n, dtype=np.int64) for o, n in w.chunks]
     return np.concatenate(parts) if parts else np.zeros(0, np.int64)
 
 
@@ -242,7 +303,7 @@ def unmasked_pairs_per_head(w: Workload) -> int:
     """Number of (query, key) pairs the mask allows, per query head and batch entry."""
     if not w.causal:
         return w.lq * w.lk
-    kpos = np.sort(np.concatenate([np.arange(n, dtype=np.int64) + o for o, n in w.chunks]))
+    kpos = np.sort(k_positions(w))
     return int(np.searchsorted(kpos, q_positions(w), side="right").sum())
 
 

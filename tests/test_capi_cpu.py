@@ -95,6 +95,16 @@ def test_ring_validation_codes(lib):
     assert _ring(lib, chunks=bad) == 2
     seg = (api.QSegment * 1)(api.QSegment(4, -1))
     assert _ring(lib, segs=seg, causal=1) == 2
+    # position steps: negative is refused; a step that carries the last key past 2^31-2 is refused
+    bad = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 8, 0, 0, 0, 64, -2))
+    assert _ring(lib, chunks=bad) == 2
+    bad = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 8, 5, 0, 0, 64, 1 << 29))
+    assert _ring(lib, chunks=bad) == 2
+    assert b"positions" in lib.ra_last_error()
+    seg = (api.QSegment * 1)(api.QSegment(4, 0, -1))
+    assert _ring(lib, segs=seg) == 2
+    seg = (api.QSegment * 1)(api.QSegment(4, 3, 1 << 30))
+    assert _ring(lib, segs=seg, causal=1) == 2
     assert _ring(lib, out=None) == 1
     assert _ring(lib, ws=None, wsb=0) == 6
     assert _ring(lib, ws=ctypes.c_void_p(0x1010), wsb=1 << 20) == 6  # misaligned

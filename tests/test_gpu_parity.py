@@ -44,16 +44,16 @@ def _check(got, ref, dtype):
 
 def _run(w, **kw):
     q, k, v, kc, vc = wl.generate_torch(w, DEV)
-    offs = [o for o, _ in w.chunks]
-    out, lse = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, return_lse=True,
-                                 scale=w.softmax_scale, **kw)
+    offs = w.kv_offsets
+    out, lse = ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, return_lse=True,
+                                 scale=w.softmax_scale, kv_position_strides=w.kv_strides, **kw)
     torch.cuda.synchronize()
     return q, kc, vc, offs, out, lse
 
 
 def _oracle(w, q, kc, vc, offs):
     return oracle.attention(q.cpu(), [c.cpu() for c in kc], [c.cpu() for c in vc], wl.q_positions(w), offs,
-                            causal=w.causal, scale=w.softmax_scale)
+                            causal=w.causal, scale=w.softmax_scale, kv_strides=w.kv_strides)
 
 
 # ---------------------------------------------------------------------------
@@ -143,14 +143,23 @@ SMALL = [
     ("bf16_d64_zigzag_gqa", "bf16", 1, 4, 2, 64, [(128, 128), (896, 128)],
      [(128 * j, 128) for j in (1, 6, 0, 7, 3, 4, 2, 5)], True),
     ("bf16_d128_nc_257", "bf16", 1, 2, 2, 128, [(0, 257)], [(0, 300), (300, 211)], False),
+    # striped shares (positions advance by P per row and per key): whole tiles per chunk (pipelined
+    # kernel with a position step), then chunks cut inside tiles (general kernel), fp32, and a split
+    ("bf16_d64_striped_p4", "bf16", 1, 4, 2, 64, [(3, 300)], [(j, 256) for j in wl.ring_order(3, 4)], True, 4),
+    ("bf16_d128_striped_p3", "bf16", 1, 2, 2, 128, [(1, 200)], [(j, 192) for j in wl.ring_order(1, 3)], True, 3),
+    ("bf16_d64_striped_ragged", "bf16", 1, 2, 2, 64, [(2, 260)], [(j, 300) for j in wl.ring_order(2, 4)], True, 4),
+    ("f32_d16_striped", "f32", 1, 2, 1, 16, [(5, 90)], [(j, 100) for j in wl.ring_order(5, 8)], True, 8),
+    ("bf16_d128_striped_split", "bf16", 1, 1, 1, 128, [(0, 150)], [(j, 2048) for j in wl.ring_order(0, 2)], True, 2),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_shares(case):
-    name, dtype, B, Hq, Hkv, d, qs, ch, causal = case
+    name, dtype, B, Hq, Hkv, d, qs, ch, causal = case[:9]
+    pstep = case[9] if len(case) > 9 else 1
     _say(name)
-    w = wl.custom(name, dtype, B, Hq, Hkv, d, qs, ch, causal, seed=zlib.crc32(name.encode()) % 1000)
+    w = wl.custom(name, dtype, B, Hq, Hkv, d, qs, ch, causal, seed=zlib.crc32(name.encode()) % 1000,
+                  pos_stride=pstep)
     q, kc, vc, offs, out, lse = _run(w)
     ref = _oracle(w, q, kc, vc, offs)
     _check(_np(out), ref["out"], dtype)
@@ -321,38 +330,37 @@ def _full(i):
     return _CACHE[i]
 
 
-@pytest.mark.parametrize("i,nrows", [(1, 512), (2, 384), (3, 384), (4, 128)])
+@pytest.mark.parametrize("i,nrows", [(1, 512), (2, 384), (3, 384), (4, 128), (5, 384)])
 def test_full_size_sampled_rows(i, nrows):
     w, (q, k, v, kc, vc) = _full(i)
     _say(f"{w.name} sampled {nrows}")
-    offs = [o for o, _ in w.chunks]
-    out, lse = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal, return_lse=True)
+    offs = w.kv_offsets
+    out, lse = ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, return_lse=True,
+                                 kv_position_strides=w.kv_strides)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     rows = wl.sample_rows(w, nrows, seed=i)
     ref = oracle.attention_rows(q.cpu(), [c.cpu() for c in kc], [c.cpu() for c in vc], rows,
-                                wl.q_positions(w), offs, causal=w.causal)
+                                wl.q_positions(w), offs, causal=w.causal, kv_strides=w.kv_strides)
     idx = tuple(np.array(rows).T)
     got = out.cpu().double().numpy()[idx]
     _check(got, ref["out"], "bf16")
     assert np.abs(lse.cpu().double().numpy()[idx] - ref["lse"]).max() <= 1e-2
     # repeat run: bit-identical
-    out2 = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal)
+    out2 = ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, kv_position_strides=w.kv_strides)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("i", [1, 3])
+@pytest.mark.parametrize("i", [1, 3, 5])
 def test_full_size_resplit_is_bit_identical(i):
     w, (q, k, v, kc, vc) = _full(i)
     _say(f"{w.name} resplit")
-    offs = [o for o, _ in w.chunks]
-    out = ra.ring_attention(q, kc, vc, w.q_segments, offs, causal=w.causal)
+    out = ra.ring_attention(q, kc, vc, w.q_runs, w.kv_offsets, causal=w.causal, kv_position_strides=w.kv_strides)
     cuts = [1000, 4096 + 3096, 5 * 4096 + 77, w.lk // 2 + 1]
     r = wl.resplit(w, cuts)
-    kc2 = [k[:, :, o:o + n] for o, n in r.chunks]
-    vc2 = [v[:, :, o:o + n] for o, n in r.chunks]
-    out2 = ra.ring_attention(q, kc2, vc2, w.q_segments, [o for o, _ in r.chunks], causal=w.causal)
+    kc2, vc2 = wl.chunk_views(r, k, v)
+    out2 = ra.ring_attention(q, kc2, vc2, r.q_runs, r.kv_offsets, causal=w.causal, kv_position_strides=r.kv_strides)
     torch.cuda.synchronize()
     assert len(r.chunks) > len(w.chunks)
     assert torch.equal(out, out2)

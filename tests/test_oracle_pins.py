@@ -355,3 +355,44 @@ def test_matches_torch_sdpa_float64(causal):
     mask = torch.from_numpy(np.arange(n)[None, :] <= qpos[:, None]) if causal else None
     ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), tk, tv, attn_mask=mask)
     assert np.max(np.abs(got - ref.numpy())) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# striped shares (glossary "ring attention", paragraph Variants: striped attention): device r of P
+# owns positions r, r+P, r+2P, ...; its result must be those rows of ordinary causal attention over
+# the whole sequence in natural order
+
+
+@pytest.mark.parametrize("P,r", [(4, 0), (4, 3), (3, 1)])
+def test_striped_share_equals_rows_of_whole_sequence_causal_sdpa(P, r):
+    torch = pytest.importorskip("torch")
+    from ring_attention_chunk_amd import workloads as wl
+
+    n, H, d = 24, 2, 8
+    q_all = _rand((1, H, n, d), 141 + P)
+    k_all = _rand((1, H, n, d), 151 + P) * 1.3
+    v_all = _rand((1, H, n, d), 161 + P)
+    # the whole sequence, unsharded, by the library routine with its built-in causal mask
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q_all), torch.from_numpy(k_all), torch.from_numpy(v_all), is_causal=True).numpy()
+    L = n // P
+    order = wl.ring_order(r, P)
+    kc = [k_all[:, :, j::P] for j in order]
+    vc = [v_all[:, :, j::P] for j in order]
+    qpos = r + P * np.arange(L)
+    got = attention(q_all[:, :, r::P], kc, vc, q_positions=qpos, kv_offsets=order, causal=True,
+                    kv_strides=[P] * P)["out"]
+    fold = ring_attention_fold(q_all[:, :, r::P], kc, vc, q_positions=qpos, kv_offsets=order, causal=True,
+                               kv_strides=[P] * P)[0]
+    assert np.max(np.abs(got - ref[:, :, r::P])) <= 1e-12
+    assert np.max(np.abs(fold - ref[:, :, r::P])) <= 1e-12
+    # the same keys read as contiguous runs would be a different (wrong) mask
+    wrong = attention(q_all[:, :, r::P], kc, vc, q_positions=qpos, kv_offsets=order, causal=True)["out"]
+    assert np.max(np.abs(wrong - ref[:, :, r::P])) > 1e-3
+
+
+def test_strided_key_positions_closed_form():
+    assert key_positions([3, 2], [5, 0], [4, 7]).tolist() == [5, 9, 13, 0, 7]
+    from oracle import query_positions
+
+    assert query_positions([(2, 3, 5), (1, 2)]).tolist() == [2, 7, 12, 1, 2]

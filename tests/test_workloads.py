@@ -97,3 +97,32 @@ def test_sample_rows_cover_segment_ends():
     assert {0, 4095, 4096, 8191} <= r
     assert len(rows) == 300
     assert all(0 <= b < w.batch and 0 <= h < w.q_heads and 0 <= i < w.lq for b, h, i in rows)
+
+
+def test_striped_share_bookkeeping():
+    w = wl.causal_striped()
+    P, L = 8, 8192
+    assert w.pos_stride == P and w.q_segments == [(5, L)]
+    assert [o for o, _ in w.chunks] == wl.ring_order(5, P)
+    kpos = wl.k_positions(w)
+    assert np.array_equal(np.sort(kpos), np.arange(P * L))  # every position once
+    assert np.array_equal(wl.q_positions(w), 5 + P * np.arange(L))
+    # query i (position 5 + 8i) sees i+1 keys of each shard j <= 5 and i keys of shards 6, 7
+    i = np.arange(L)
+    assert wl.unmasked_pairs_per_head(w) == int(((5 + 1) * (i + 1) + 2 * i).sum())
+
+
+def test_striped_generation_holds_each_shard_contiguously():
+    w = wl.custom("s", "f32", 1, 1, 1, 4, [(1, 5)], [(j, 6) for j in wl.ring_order(1, 3)], True, pos_stride=3)
+    q, k, v = wl.generate_numpy(w)
+    tq, tk, tv, kc, vc = wl.generate_torch(w)
+    for (o, n), c in zip(w.chunks, kc):
+        assert np.array_equal(c.numpy(), k[:, :, o:o + 3 * (n - 1) + 1:3])
+    # queries are the rows at positions 1, 4, 7, ... of the whole sequence's seeded values
+    full_q = wl._normal_positions(w.seed, 0, (1, 1), 0, 18, 4)
+    assert np.array_equal(q, full_q[:, :, 1:14:3])
+    # a re-split keeps every key in place
+    r = wl.resplit(w, [2, 9, 13])
+    kc2, _ = wl.chunk_views(r, tk, tv)
+    assert np.array_equal(np.concatenate([c.numpy() for c in kc2], 2), np.concatenate([c.numpy() for c in kc], 2))
+    assert np.array_equal(wl.k_positions(r), wl.k_positions(w))
