@@ -1103,9 +1103,10 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 // keys of a tile have positions pos0 + kps * key in one arithmetic progression
 // (kps = 1 for contiguous shards): key `key` is masked for the lane's query
 // when key > min(floor((qpos - pos0) / kps), keys in the tile - 1). MASK
-// selects the variant that applies it to every tile; without it no tile needs
-// one (no causal mask and a whole number of tiles).
-template <int DP, int MODE, bool MASK>
+// selects the variant that applies it to every tile (1: kps = 1; 2: any kps,
+// at the cost of an integer division per lane and step); with MASK = 0 no
+// tile needs one (no causal mask and a whole number of tiles).
+template <int DP, int MODE, int MASK>
 __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void attention_bf16_kernel(Params p) {
   constexpr int W = pipe_waves(MODE);
   constexpr int kPipeThreads = 64 * W;
@@ -1324,7 +1325,7 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
   auto key_bound = [&](int t, int pos0) {
     const int nvalid = (int)min((int64_t)TB, p.Lk - (int64_t)t * TB);
     int rel = wk.qpos < pos0 ? -1 : wk.qpos - pos0;
-    if (p.kps != 1) rel = rel < 0 ? -1 : rel / p.kps;  // uniform: striped positions only
+    if constexpr (MASK == 2) rel = rel < 0 ? -1 : rel / p.kps;  // striped positions
     return min(rel, nvalid - 1) - 4 * h;
   };
   auto mask_tile = [&](f32x16* s, int bound) {
@@ -1629,10 +1630,14 @@ hipError_t launch_t(const Params& p, int nblocks, hipStream_t s) {
 template <int DP, int MODE>
 hipError_t launch_pipe(const Params& p, bool mask, int nblocks, hipStream_t s) {
   constexpr int nt = 64 * pipe_waves(MODE);
-  if (mask)
-    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, true>), dim3(nblocks), dim3(nt), 0, s, p);
-  else
-    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, false>), dim3(nblocks), dim3(nt), 0, s, p);
+  if (mask && MODE == kRingCausal && p.kps != 1) {
+    if constexpr (MODE == kRingCausal)
+      hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, 2>), dim3(nblocks), dim3(nt), 0, s, p);
+  } else if (mask) {
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, 1>), dim3(nblocks), dim3(nt), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, 0>), dim3(nblocks), dim3(nt), 0, s, p);
+  }
   return hipGetLastError();
 }
 
