@@ -115,6 +115,7 @@ struct Params {
   int nsplit;   // key-tile ranges per (batch, head, query tile)
   int vec;      // 16-byte loads allowed for q, k and v
   int kps;      // position step shared by every chunk (pipelined causal path only)
+  double kinv;  // 1 / kps
   float scale;  // softmax scale
   float c2;     // scale * log2(e)
 };
@@ -207,13 +208,11 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
         cc = chunk_at<MODE>(p, c);
       }
       if (kmin > qmax) {
-        // nothing here is visible; if the whole chunk is in the future, jump past it
-        if (one && ch.pos0 > qmax) {
-          const int nt = (int)((ch.start + ch.len) / TB);
-          t = nt > t ? nt : t + 1;
-        } else {
-          ++t;
-        }
+        // nothing here is visible, and positions only grow along a chunk, so
+        // no later key of chunk `cursor` is visible either: go on at the tile
+        // that holds the chunk's end
+        const int nt = (int)((ch.start + ch.len) / TB);
+        t = nt > t ? nt : t + 1;
         continue;
       }
     }
@@ -1104,7 +1103,7 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 // (kps = 1 for contiguous shards): key `key` is masked for the lane's query
 // when key > min(floor((qpos - pos0) / kps), keys in the tile - 1). MASK
 // selects the variant that applies it to every tile (1: kps = 1; 2: any kps,
-// at the cost of an integer division per lane and step); with MASK = 0 no
+// at the cost of an fp64 multiply per lane and step); with MASK = 0 no
 // tile needs one (no causal mask and a whole number of tiles).
 template <int DP, int MODE, int MASK>
 __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void attention_bf16_kernel(Params p) {
@@ -1325,7 +1324,10 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
   auto key_bound = [&](int t, int pos0) {
     const int nvalid = (int)min((int64_t)TB, p.Lk - (int64_t)t * TB);
     int rel = wk.qpos < pos0 ? -1 : wk.qpos - pos0;
-    if constexpr (MASK == 2) rel = rel < 0 ? -1 : rel / p.kps;  // striped positions
+    // floor(rel / kps) for 0 <= rel < 2^31 as (rel + 1/2) / kps in fp64: the
+    // exact quotient lies at least 1/(2 kps) from an integer, and the product's
+    // error is below 2^31 / kps * 2^-51, so truncation gives the floor exactly
+    if constexpr (MASK == 2) rel = rel < 0 ? -1 : (int)__builtin_fma((double)rel, p.kinv, 0.5 * p.kinv);
     return min(rel, nvalid - 1) - 4 * h;
   };
   auto mask_tile = [&](f32x16* s, int bound) {
@@ -1848,6 +1850,7 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.nsplit = 1;
   p.vec = vec;
   p.kps = kps;
+  p.kinv = 1.0 / kps;
   p.scale = scale;
   p.c2 = scale * kLog2e;
   const bool mask = chunk->len % pipe_tile(dp_of(head_dim)) != 0;
@@ -1987,6 +1990,7 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   p.nsplit = nsplit;
   p.vec = vec && vec_ok(q, head_dim, head_dim, elem);
   p.kps = kps;
+  p.kinv = 1.0 / kps;
   p.scale = scale;
   p.c2 = scale * kLog2e;
   const bool mask = causal || lk % pipe_tile(dp_of(head_dim)) != 0;
