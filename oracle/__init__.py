@@ -14,6 +14,11 @@ Two independent statements of what the method computes live here:
   the oracle for ``ring_attention`` is that ordinary attention, with the
   causal mask taken from global positions ("Ring Attention: Distributed Reads
   with Online Softmax", section "Causal masks depend on global positions").
+* :mod:`oracle.backward` -- the gradients of that ordinary attention (dQ,
+  and dK, dV summed per key over every query that sees it), written out from
+  the chain rule ("Ring Attention: Distributed Reads with Online Softmax",
+  section "Backward must aggregate shared dependencies"). It is pinned by
+  central finite differences of :mod:`oracle.direct` and by torch autograd.
 * :mod:`oracle.online_softmax` -- the exercise's three functions written out
   in fp64 (chunk statistics, the rescale-to-shared-max merge, and the fold
   over chunks followed by one normalisation). It is the reference for the
@@ -25,11 +30,13 @@ against the pages' worked example, closed forms, brute force on tiny inputs
 and a library special case; no function is "parity unpinned".
 """
 
+from .backward import attention_backward
 from .direct import attention, attention_rows, key_positions, query_positions
 from .online_softmax import chunk_stats, merge_chunk_stats, ring_attention_fold, normalize
 
 __all__ = [
     "attention",
+    "attention_backward",
     "attention_rows",
     "key_positions",
     "query_positions",
