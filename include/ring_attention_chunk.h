@@ -148,11 +148,54 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
                       void* workspace, size_t workspace_bytes, float* out, float* lse,
                       void* stream);
 
+/* Device workspace, in bytes, that ra_ring_attention_backward needs: the
+ * chunk table, the query and key positions (4 bytes per query row and per
+ * key), per-32-row position bounds, and delta (fp32 per (batch, head, query)
+ * row). A multiple of 256. */
+size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int64_t q_len, int64_t total_keys, int n_chunks);
+
+/* Gradients of ring_attention for this device's share.
+ * "Ring Attention: Distributed Reads with Online Softmax", section "Backward
+ * must aggregate shared dependencies": the local queries contribute gradients
+ * to the keys and values of every chunk they attend to; these are summed per
+ * key and returned per chunk, for the chunk's owner to add to the
+ * contributions of the other devices. Probabilities are recomputed from the
+ * forward's lse with the same scale and the same global-position causal mask.
+ * With p_ij = exp(scale <q_i, k_j> - lse_i) over allowed pairs and
+ * delta_i = <dout_i, out_i>:
+ *   dv_j = sum_i p_ij dout_i,  ds_ij = p_ij (<dout_i, v_j> - delta_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ * where the sums over i run over every query head sharing k_j's head (GQA).
+ *  dtype       RA_BF16 only (bf16 matrix cores, fp32 accumulation); other
+ *              types return RA_ERR_UNSUPPORTED. head_dim is 32, 64 or 128.
+ *  q, dout     [B,Hq,q_len,d] bf16; out [B,Hq,q_len,d] fp32 and lse
+ *              [B,Hq,q_len] fp32 as ra_ring_attention returned them for the
+ *              same inputs (lse must not be NULL there).
+ *  q_segments, chunks, causal, scale: as for ra_ring_attention; rows of
+ *              every chunk must be 16-byte aligned.
+ *  dq          [B,Hq,q_len,d] fp32 (written).
+ *  dk, dv      [B,Hkv,total_keys,d] fp32 (written): key j of the
+ *              concatenated chunk list in list order, so chunk c's gradient
+ *              is the slice of its keys. Every row is written, zero for keys
+ *              no local query sees.
+ *  workspace   >= ra_ring_backward_workspace_bytes(...) bytes, 256-byte
+ *              aligned; tables are copied there on `stream`.
+ * Outputs must not overlap inputs. The result is bit-identical from run to
+ * run (no atomics; every sum in a fixed order). */
+int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, int head_dim,
+                               const void* q, const ra_q_segment* q_segments, int n_q_segments,
+                               const ra_kv_chunk* chunks, int n_chunks, int causal, float scale,
+                               const float* out, const float* lse, const void* dout,
+                               void* workspace, size_t workspace_bytes,
+                               float* dq, float* dk, float* dv, void* stream);
+
 /* Measurement aid, outside the pages' API: device time of the attention
  * kernels themselves. While enabled, every ra_ring_attention and
  * ra_attention_chunk_stats call records a pair of HIP events on its stream,
  * immediately before and after its attention kernel (the key-range combine
  * of ra_ring_attention is outside the pair); up to 512 pairs are kept.
+ * Each ra_ring_attention_backward call records two pairs: one around its
+ * dK/dV kernel and one around its dQ kernel.
  * ra_kernel_timer(1) creates the events on first use (the only resources the
  * library ever creates; they live until the process ends), clears the kept
  * pairs and enables recording; ra_kernel_timer(0) disables it.

@@ -1,7 +1,8 @@
 """MI355X (gfx950) ring attention on one device's share: HIP kernels behind a C ABI.
 
-``attention_chunk_stats``, ``merge_chunk_stats`` and ``ring_attention`` call the
-HIP library through ctypes (see ``api.py``); ``workloads`` builds the seeded
+``attention_chunk_stats``, ``merge_chunk_stats``, ``ring_attention`` and
+``ring_attention_backward`` call the HIP library through ctypes (see
+``api.py``); ``workloads`` builds the seeded
 synthetic shares used by the tests and the benchmark.
 """
 
@@ -12,6 +13,7 @@ from .api import (
     load_library,
     merge_chunk_stats,
     ring_attention,
+    ring_attention_backward,
 )
 
 __all__ = [
@@ -21,4 +23,5 @@ __all__ = [
     "load_library",
     "merge_chunk_stats",
     "ring_attention",
+    "ring_attention_backward",
 ]

@@ -27,6 +27,8 @@ EXPORTS = (
     "ra_merge_chunk_stats",
     "ra_ring_workspace_bytes",
     "ra_ring_attention",
+    "ra_ring_backward_workspace_bytes",
+    "ra_ring_attention_backward",
     "ra_kernel_timer",
     "ra_kernel_timer_read",
     "ra_status_string",
@@ -79,6 +81,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_ring_attention.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                       ctypes.POINTER(KVChunk), i32, i32, f32, vp, sz, vp, vp, vp]
     lib.ra_ring_attention.restype = i32
+    lib.ra_ring_backward_workspace_bytes.argtypes = [i32, i32, i64, i64, i32]
+    lib.ra_ring_backward_workspace_bytes.restype = sz
+    lib.ra_ring_attention_backward.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
+                                               ctypes.POINTER(KVChunk), i32, i32, f32, vp, vp, vp, vp, sz, vp, vp,
+                                               vp, vp]
+    lib.ra_ring_attention_backward.restype = i32
     lib.ra_kernel_timer.argtypes = [i32]
     lib.ra_kernel_timer.restype = i32
     lib.ra_kernel_timer_read.argtypes = [ctypes.POINTER(f32), ctypes.POINTER(i32)]
@@ -291,3 +299,92 @@ def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global
                                out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q))
     _check(lib, st, "ring_attention")
     return (out, lse) if return_lse else out
+
+
+def _marshal(query, key_chunks, value_chunks, q_global_offset, kv_global_offsets, kv_position_strides):
+    """Shared argument checks of the ring calls: descriptors and query runs."""
+    if len(key_chunks) != len(value_chunks):
+        raise RingAttentionError("key_chunks and value_chunks differ in length")
+    _require_gpu(query, *key_chunks, *value_chunks)
+    if query.dim() != 4:
+        raise RingAttentionError("query must be [batch, q_heads, q_len, head_dim]")
+    B, Hq, Lq, d = query.shape
+    for t in list(key_chunks) + list(value_chunks):
+        if t.dtype != query.dtype:
+            raise RingAttentionError("query, keys and values must share a dtype")
+    if kv_global_offsets is None:
+        kv_global_offsets, acc = [], 0
+        for k in key_chunks:
+            kv_global_offsets.append(acc)
+            acc += int(k.shape[2])
+    if len(kv_global_offsets) != len(key_chunks):
+        raise RingAttentionError("one global offset per chunk is required")
+    if kv_position_strides is None:
+        kv_position_strides = [1] * len(key_chunks)
+    if len(kv_position_strides) != len(key_chunks):
+        raise RingAttentionError("one position stride per chunk is required")
+    Hkv = int(key_chunks[0].shape[1]) if key_chunks else Hq
+    n = len(key_chunks)
+    descs = (KVChunk * max(n, 1))()
+    for i, (k, v, off, ps) in enumerate(zip(key_chunks, value_chunks, kv_global_offsets, kv_position_strides)):
+        descs[i] = _chunk_desc(k, v, off, B, Hkv, d, ps)
+    if isinstance(q_global_offset, int):
+        segs_py = [(int(q_global_offset), Lq, 1)]
+    else:
+        segs_py = [(int(g[0]), int(g[1]), int(g[2]) if len(g) > 2 else 1) for g in q_global_offset]
+    if sum(g[1] for g in segs_py) != Lq:
+        raise RingAttentionError(f"query segments cover {sum(g[1] for g in segs_py)} rows, query has {Lq}")
+    segs = (QSegment * len(segs_py))(*[QSegment(n_, o, ps) for o, n_, ps in segs_py])
+    return Hkv, descs, n, segs, len(segs_py)
+
+
+def ring_attention_backward(query, key_chunks: Sequence, value_chunks: Sequence, out, lse, dout,
+                            q_global_offset: QOffset = 0, kv_global_offsets: Optional[Sequence[int]] = None,
+                            causal: bool = False, scale: Optional[float] = None,
+                            kv_position_strides: Optional[Sequence[int]] = None, workspace=None):
+    """Gradients of :func:`ring_attention` for this share: ``(dq, dk_chunks, dv_chunks)``.
+
+    ``out`` and ``lse`` are what ``ring_attention(..., return_lse=True)``
+    returned for the same inputs; ``dout`` is the gradient of the output (same
+    dtype as the query; bf16 only). ``dq`` is [B, Hq, Lq, d] fp32; ``dk_chunks``
+    and ``dv_chunks`` hold, per chunk, this share's contribution to that
+    chunk's key and value gradients, [B, Hkv, len, d] fp32 each (views of one
+    buffer in list order).
+    """
+    torch = _torch()
+    lib = load_library()
+    Hkv, descs, n, segs, nseg = _marshal(query, key_chunks, value_chunks, q_global_offset, kv_global_offsets,
+                                         kv_position_strides)
+    q = query.contiguous()
+    B, Hq, Lq, d = q.shape
+    _require_gpu(out, lse, dout)
+    if dout.dtype != q.dtype or tuple(dout.shape) != tuple(q.shape):
+        raise RingAttentionError("dout must have the query's shape and dtype")
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape):
+        raise RingAttentionError("out must be the fp32 output of ring_attention")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Lq):
+        raise RingAttentionError("lse must be the fp32 [B, Hq, Lq] log-sum-exp of ring_attention")
+    do, o, ls = dout.contiguous(), out.contiguous(), lse.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lens = [int(k.shape[2]) for k in key_chunks]
+    total = sum(lens)
+    need = lib.ra_ring_backward_workspace_bytes(B, Hq, Lq, total, n)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() < need or workspace.data_ptr() % 256 != 0:
+        raise RingAttentionError(f"workspace must hold {need} bytes at a 256-byte aligned address")
+    dq = torch.empty((B, Hq, Lq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Hkv, total, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Hkv, total, d), dtype=torch.float32, device=q.device)
+    st = lib.ra_ring_attention_backward(_dtype_code(q), B, Hq, Hkv, d, q.data_ptr(), segs, nseg, descs, n,
+                                        int(bool(causal)), float(scale), o.data_ptr(), ls.data_ptr(),
+                                        do.data_ptr(), workspace.data_ptr(), workspace.numel(), dq.data_ptr(),
+                                        dk.data_ptr(), dv.data_ptr(), _stream(q))
+    _check(lib, st, "ring_attention_backward")
+    starts = [0]
+    for ln in lens:
+        starts.append(starts[-1] + ln)
+    dks = [dk[:, :, a:a + ln] for a, ln in zip(starts, lens)]
+    dvs = [dv[:, :, a:a + ln] for a, ln in zip(starts, lens)]
+    return dq, dks, dvs

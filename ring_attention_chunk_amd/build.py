@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libring_attention_chunk.so")
-SOURCES = [os.path.join(PKG, "csrc", "attention.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "attention.hip"), os.path.join(PKG, "csrc", "backward.hip")]
 
 # Packed fp32 instructions are left to nobody: the feature is switched off for
 # every HIP compilation of this library.

@@ -48,6 +48,7 @@
 #include <string.h>
 
 #include "ring_attention_chunk.h"
+#include "host_common.h"
 
 namespace {
 
@@ -1540,8 +1541,13 @@ __global__ __launch_bounds__(256) void merge_kernel(int64_t rows, int d, int lpr
   }
 }
 
+}  // namespace
+
 // ---------------------------------------------------------------------------
-// Host side: validation, descriptor tables, dispatch.
+// Host side: validation, descriptor tables, dispatch. The helpers in ra_host
+// are shared with the backward pass (host_common.h).
+
+namespace ra_host {
 
 thread_local char g_err[512] = "";
 
@@ -1555,8 +1561,6 @@ int fail(int code, const char* fmt, ...) {
 }
 
 int hip_fail(hipError_t e, const char* what) { return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e)); }
-
-constexpr int64_t kPosLimit = 0x7ffffffeLL;
 
 int check_dims(int dtype, int batch, int q_heads, int kv_heads, int head_dim) {
   if (dtype != RA_F32 && dtype != RA_BF16) return fail(RA_ERR_DTYPE, "unknown dtype %d", dtype);
@@ -1603,6 +1607,11 @@ bool chunk_vec_ok(const ra_kv_chunk& c, int head_dim, int64_t elem) {
   return vec_ok(c.k, c.stride_s, head_dim, elem) && vec_ok(c.v, c.stride_s, head_dim, elem) &&
          c.stride_b % per16 == 0 && c.stride_h % per16 == 0;
 }
+
+}  // namespace ra_host
+
+namespace {
+using namespace ra_host;
 
 int dp_of(int head_dim) { return head_dim <= 32 ? 32 : (head_dim <= 64 ? 64 : 128); }
 
@@ -1752,10 +1761,13 @@ size_t ra_ring_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_l
 }
 
 // ---------------------------------------------------------------------------
+}  // extern "C"
+
 // Measurement hook: HIP events recorded on the call's stream right before and
 // after the attention kernel of each ring_attention / attention_chunk_stats
-// call (not around the key-range combine), while enabled.
-namespace {
+// call (not around the key-range combine), and around the two gradient
+// kernels of each ring_attention_backward call, while enabled.
+namespace ra_host {
 constexpr int kTimerSlots = 512;
 hipEvent_t g_tev[2][kTimerSlots];
 bool g_tev_made = false;
@@ -1767,7 +1779,9 @@ void timer_begin(hipStream_t s) {
 void timer_end(hipStream_t s) {
   if (g_timer_on && g_timer_n < kTimerSlots) (void)hipEventRecord(g_tev[1][g_timer_n++], s);
 }
-}  // namespace
+}  // namespace ra_host
+
+extern "C" {
 
 int ra_kernel_timer(int enable) {
   g_err[0] = 0;

@@ -1,0 +1,620 @@
+// backward.hip -- gradients of ring attention for one device's share (gfx950).
+//
+// What is computed ("Ring Attention: Distributed Reads with Online Softmax",
+// section "Backward must aggregate shared dependencies"): the local queries
+// contribute gradients to the keys and values of every chunk they attend to;
+// the contributions to one key are summed (over all local queries and, with
+// GQA, over the query heads sharing its key/value head) and handed back per
+// chunk, to be returned to the chunk's owner. Probability tiles are recomputed
+// from the forward's log-sum-exp with the same scale and the same global-
+// position causal mask as the forward pass. With p = exp(s - lse) and
+// delta_i = <dO_i, out_i>:
+//   dV_j = sum_i p_ij dO_i,   dS_ij = p_ij (<dO_i, v_j> - delta_i),
+//   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
+//
+// Mapping onto the chip
+// ---------------------
+//  * delta_kernel: one pass over dO and out (HBM-bound).
+//  * dkdv_kernel: a workgroup owns 128 keys of one (batch, kv head), 32 per
+//    wave, and walks every query row of every query head of its group in
+//    blocks of 32. K and V stay in registers as MFMA B operands; each query
+//    block (Q, dO, their transposes, lse, delta, positions) is staged once in
+//    LDS for the four waves. S = Q K^T and dP = dO V^T put one key per lane and
+//    16 queries in its registers; those registers, rounded to bf16, are
+//    directly the B operand of dV^T += dO^T P and dK^T += Q^T dS, whose A
+//    operands read the transposed tiles in the same (permuted) query order.
+//  * dq_kernel: a workgroup owns 128 query rows of one (batch, head), 32 per
+//    wave, and walks the keys in tiles of 32. Q and dO stay in registers;
+//    S^T = K Q^T and dP^T = V dO^T put one query per lane; dQ^T += K^T dS^T.
+//  * Both gradient kernels give every output row to exactly one lane and sum
+//    in a fixed order: no atomics, bit-reproducible results.
+//  * Query blocks that lie before every key of a workgroup, and key tiles that
+//    lie after every query of a workgroup, are skipped (causal).
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "host_common.h"
+#include "ring_attention_chunk.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kRows = 32;                    // rows per MFMA block (keys or queries)
+constexpr int kGroupRows = kRows * kBwdWaves;  // rows per workgroup
+constexpr int kPosMax = 0x7fffffff;          // position of a missing key: after everything
+constexpr int kPosAllQ = 0x7ffffffe;         // query position that sees every real key
+constexpr int kPosMinQ = -0x7fffffff - 1;    // position of a missing query row: sees nothing
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdChunk {
+  const void* k;
+  const void* v;
+  int64_t start;  // index of the chunk's first key in the concatenated list
+  int64_t len;
+  int64_t sb, sh, ss;
+  int32_t pos0, ps;
+};
+
+struct BwdParams {
+  const __bf16* q;     // [B, Hq, Lq, d]
+  const __bf16* dout;  // [B, Hq, Lq, d]
+  const float* out;    // [B, Hq, Lq, d]
+  const float* lse;    // [B, Hq, Lq]
+  float* delta;        // [B, Hq, Lq] (workspace)
+  const int* qpos;     // [Lq] query positions (kPosAllQ when not causal)
+  const int* kpos;     // [Lk] key positions in list order
+  const int* qblk_max; // [ceil(Lq / 32)] largest query position of each 32-row block
+  const int* ktile_min;// [ceil(Lk / 32)] smallest key position of each 32-key tile
+  const BwdChunk* chunks;
+  float* dq;           // [B, Hq, Lq, d]
+  float* dk;           // [B, Hkv, Lk, d]
+  float* dv;           // [B, Hkv, Lk, d]
+  int64_t Lq, Lk;
+  int n_chunks;
+  int B, Hq, Hkv, d;
+  int causal;
+  float scale;
+  float c2;  // scale * log2(e)
+};
+
+// Row address of key j (chunk `c` holds it); the cursor only moves forward.
+__device__ __forceinline__ int64_t key_offset(const BwdParams& p, int64_t j, int b, int hk, int& c) {
+  while (c + 1 < p.n_chunks && j >= p.chunks[c].start + p.chunks[c].len) ++c;
+  const BwdChunk& ch = p.chunks[c];
+  return (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j - ch.start) * ch.ss;
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& x, int t) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[8 * t + i];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// delta_i = <dO_i, out_i>: DP/8 lanes per row, 16-byte loads of dO.
+
+__global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int d, int lpr, int lpr_shift,
+                                                    const __bf16* __restrict__ dout, const float* __restrict__ out,
+                                                    float* __restrict__ delta) {
+  const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> lpr_shift;
+  const int sub = threadIdx.x & (lpr - 1);
+  float acc = 0.f;
+  if (r < rows) {
+    for (int c = sub * 8; c < d; c += lpr * 8) {
+      const u32x4 raw = *(const u32x4*)(dout + r * d + c);
+      const bf16x8 g = __builtin_bit_cast(bf16x8, raw);
+      const f32x4 o0 = *(const f32x4*)(out + r * d + c);
+      const f32x4 o1 = *(const f32x4*)(out + r * d + c + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf((float)g[i], o0[i], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf((float)g[4 + i], o1[i], acc);
+    }
+  }
+  for (int o = lpr >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (r < rows && sub == 0) delta[r] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Staging of a 32-row block of a [rows, d] bf16 tensor into LDS, row-major
+// (row stride DP + 8 elements) and transposed (row stride 32 + 4 elements).
+// Rows at or past `nrows` and columns past d are zero.
+
+template <int DP>
+struct Tile {
+  static constexpr int RS = DP + 8;       // row-major stride (elements)
+  static constexpr int TS = kRows + 4;    // transposed stride (elements)
+  static constexpr int PIECES = kRows * DP / 8;
+
+  static __device__ __forceinline__ void stage(const __bf16* src, int64_t nrows, int d, __bf16* rm, __bf16* tr,
+                                               int tid) {
+    for (int pc = tid; pc < PIECES; pc += kBwdThreads) {
+      const int r = pc / (DP / 8), c8 = pc % (DP / 8);
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (r < nrows && c8 * 8 < d) raw = *(const u32x4*)(src + (int64_t)r * d + c8 * 8);
+      *(u32x4*)(rm + r * RS + c8 * 8) = raw;
+      const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tr[(c8 * 8 + i) * TS + r] = v[i];
+    }
+  }
+
+  // A operand of a 32x32x16 MFMA from the row-major tile: row lane % 32, k = 16 s + 8 h .. +7.
+  static __device__ __forceinline__ bf16x8 rows_frag(const __bf16* rm, int lane, int s) {
+    return *(const bf16x8*)(rm + (lane & 31) * RS + 16 * s + 8 * (lane >> 5));
+  }
+
+  // A operand from the transposed tile: row db * 32 + lane % 32 (a column of the block), and the
+  // k slots in the order of an MFMA output's registers 8t .. 8t+7: rows 16t + 4h .. +3 and
+  // 16t + 8 + 4h .. +3 of the block.
+  static __device__ __forceinline__ bf16x8 cols_frag(const __bf16* tr, int lane, int db, int t) {
+    const __bf16* row = tr + (db * 32 + (lane & 31)) * TS + 16 * t + 4 * (lane >> 5);
+    const bf16x4 a = *(const bf16x4*)row;
+    const bf16x4 b = *(const bf16x4*)(row + 8);
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+};
+
+// Output register r of a 32x32 MFMA block sits at row 8 (r / 4) + 4 h + r % 4.
+__device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// ---------------------------------------------------------------------------
+// dK and dV of 128 keys per workgroup.
+
+template <int DP>
+__global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
+  using T = Tile<DP>;
+  constexpr int NS = DP / 16;  // k-steps over head_dim
+  constexpr int NB = DP / 32;  // 32-row blocks of head_dim
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[kRows * T::RS];
+  __shared__ __attribute__((aligned(16))) __bf16 QTs[DP * T::TS];
+  __shared__ __attribute__((aligned(16))) __bf16 Gs[kRows * T::RS];
+  __shared__ __attribute__((aligned(16))) __bf16 GTs[DP * T::TS];
+  __shared__ float lse2s[kRows], dels[kRows];
+  __shared__ int qps[kRows];
+  __shared__ int kmin_red[kBwdWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int n_kt = (int)((p.Lk + kGroupRows - 1) / kGroupRows);
+  const int kt = blockIdx.x % n_kt;
+  const int bh = blockIdx.x / n_kt;
+  const int hk = bh % p.Hkv, b = bh / p.Hkv;
+  const int group = p.Hq / p.Hkv;
+
+  // this lane's key: its K and V rows as B operands, and its position
+  const int64_t j = (int64_t)kt * kGroupRows + wave * kRows + (lane & 31);
+  const bool kvalid = j < p.Lk;
+  bf16x8 kf[NS], vf[NS];
+  int kp = kPosMax;
+  {
+    int c = 0;
+    const int64_t off = kvalid ? key_offset(p, j, b, hk, c) : 0;
+    const __bf16* kr = (const __bf16*)p.chunks[c].k + off;
+    const __bf16* vr = (const __bf16*)p.chunks[c].v + off;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int col = 16 * s + 8 * h;
+      u32x4 kraw = {0u, 0u, 0u, 0u}, vraw = {0u, 0u, 0u, 0u};
+      if (kvalid && col < p.d) {
+        kraw = *(const u32x4*)(kr + col);
+        vraw = *(const u32x4*)(vr + col);
+      }
+      kf[s] = __builtin_bit_cast(bf16x8, kraw);
+      vf[s] = __builtin_bit_cast(bf16x8, vraw);
+    }
+    if (kvalid) kp = p.kpos[j];
+  }
+  // smallest key position of the workgroup: query blocks entirely before it see nothing here
+  int wk = kp;
+  for (int o = 32; o > 0; o >>= 1) wk = min(wk, __shfl_xor(wk, o));
+  if (lane == 0) kmin_red[wave] = wk;
+  __syncthreads();
+  int kmin = kmin_red[0];
+  for (int w = 1; w < kBwdWaves; ++w) kmin = min(kmin, kmin_red[w]);
+
+  f32x16 dkT[NB], dvT[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    dkT[i] = f32x16{};
+    dvT[i] = f32x16{};
+  }
+
+  const int n_qb = (int)((p.Lq + kRows - 1) / kRows);
+  for (int g = 0; g < group; ++g) {
+    const int hq = hk * group + g;
+    const int64_t rowbase = ((int64_t)b * p.Hq + hq) * p.Lq;
+    for (int qb = 0; qb < n_qb; ++qb) {
+      if (p.causal && p.qblk_max[qb] < kmin) continue;  // uniform
+      const int64_t r0 = (int64_t)qb * kRows;
+      const int64_t nrows = min((int64_t)kRows, p.Lq - r0);
+      __syncthreads();  // previous block's LDS reads are done
+      T::stage(p.q + (rowbase + r0) * p.d, nrows, p.d, Qs, QTs, tid);
+      T::stage(p.dout + (rowbase + r0) * p.d, nrows, p.d, Gs, GTs, tid);
+      if (tid < kRows) {
+        const bool v = tid < nrows;
+        const float ls = v ? p.lse[rowbase + r0 + tid] : 0.f;
+        lse2s[tid] = (ls == -INFINITY) ? 0.f : ls * kLog2e;
+        dels[tid] = v ? p.delta[rowbase + r0 + tid] : 0.f;
+        qps[tid] = v ? p.qpos[r0 + tid] : kPosMinQ;
+      }
+      __syncthreads();
+
+      // S = Q K^T and dP = dO V^T: lane holds key lane % 32 and queries out_row(r)
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Qs, lane, st), kf[st], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Gs, lane, st), vf[st], dp, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = out_row(r, lane);
+        const bool vis = kp <= qps[qi];
+        const float pr = vis ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2s[qi]) : 0.f;
+        s[r] = pr;
+        dp[r] = pr * (dp[r] - dels[qi]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pf = to_bf16x8(s, t);
+        const bf16x8 df = to_bf16x8(dp, t);
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(GTs, lane, db, t), pf, dvT[db], 0, 0, 0);
+          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(QTs, lane, db, t), df, dkT[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // lane writes its key's row: block db, registers 4i .. 4i+3 are columns db*32 + 8i + 4h .. +3
+  if (kvalid) {
+    float* dkr = p.dk + (((int64_t)b * p.Hkv + hk) * p.Lk + j) * p.d;
+    float* dvr = p.dv + (((int64_t)b * p.Hkv + hk) * p.Lk + j) * p.d;
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = db * 32 + 8 * i + 4 * h;
+        if (col < p.d) {
+          const f32x4 kv = {dkT[db][4 * i] * p.scale, dkT[db][4 * i + 1] * p.scale, dkT[db][4 * i + 2] * p.scale,
+                            dkT[db][4 * i + 3] * p.scale};
+          const f32x4 vv = {dvT[db][4 * i], dvT[db][4 * i + 1], dvT[db][4 * i + 2], dvT[db][4 * i + 3]};
+          *(f32x4*)(dkr + col) = kv;
+          *(f32x4*)(dvr + col) = vv;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ of 128 query rows per workgroup.
+
+template <int DP>
+__global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
+  using T = Tile<DP>;
+  constexpr int NS = DP / 16;
+  constexpr int NB = DP / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kRows * T::RS];
+  __shared__ __attribute__((aligned(16))) __bf16 KTs[DP * T::TS];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[kRows * T::RS];
+  __shared__ int kps[kRows];
+  __shared__ int qmax_red[kBwdWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int n_qt = (int)((p.Lq + kGroupRows - 1) / kGroupRows);
+  const int qt = blockIdx.x % n_qt;
+  const int bh = blockIdx.x / n_qt;
+  const int hq = bh % p.Hq, b = bh / p.Hq;
+  const int hk = hq / (p.Hq / p.Hkv);
+
+  // this lane's query: Q and dO rows as B operands, lse, delta and position
+  const int64_t i = (int64_t)qt * kGroupRows + wave * kRows + (lane & 31);
+  const bool qvalid = i < p.Lq;
+  const int64_t row = ((int64_t)b * p.Hq + hq) * p.Lq + (qvalid ? i : 0);
+  bf16x8 qf[NS], gf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int col = 16 * s + 8 * h;
+    u32x4 qraw = {0u, 0u, 0u, 0u}, graw = {0u, 0u, 0u, 0u};
+    if (qvalid && col < p.d) {
+      qraw = *(const u32x4*)(p.q + row * p.d + col);
+      graw = *(const u32x4*)(p.dout + row * p.d + col);
+    }
+    qf[s] = __builtin_bit_cast(bf16x8, qraw);
+    gf[s] = __builtin_bit_cast(bf16x8, graw);
+  }
+  const float lsev = qvalid ? p.lse[row] : 0.f;
+  const float lse2 = (lsev == -INFINITY) ? 0.f : lsev * kLog2e;
+  const float del = qvalid ? p.delta[row] : 0.f;
+  const int qp = qvalid ? p.qpos[i] : kPosMinQ;
+  int wq = qp;
+  for (int o = 32; o > 0; o >>= 1) wq = max(wq, __shfl_xor(wq, o));
+  if (lane == 0) qmax_red[wave] = wq;
+  __syncthreads();
+  int qmax = qmax_red[0];
+  for (int w = 1; w < kBwdWaves; ++w) qmax = max(qmax, qmax_red[w]);
+
+  f32x16 dqT[NB];
+#pragma unroll
+  for (int db = 0; db < NB; ++db) dqT[db] = f32x16{};
+
+  // staging cursors: each thread's pieces keep their row slot from tile to tile
+  constexpr int PER = (T::PIECES + kBwdThreads - 1) / kBwdThreads;
+  int cur[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) cur[k] = 0;
+
+  const int n_kt = (int)((p.Lk + kRows - 1) / kRows);
+  for (int t = 0; t < n_kt; ++t) {
+    if (p.causal && p.ktile_min[t] > qmax) continue;  // uniform
+    const int64_t j0 = (int64_t)t * kRows;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int pc = tid + k * kBwdThreads;
+      if (pc < T::PIECES) {
+        const int r = pc / (DP / 8), c8 = pc % (DP / 8);
+        const int64_t j = j0 + r;
+        u32x4 kraw = {0u, 0u, 0u, 0u}, vraw = {0u, 0u, 0u, 0u};
+        if (j < p.Lk && c8 * 8 < p.d) {
+          const int64_t off = key_offset(p, j, b, hk, cur[k]);
+          kraw = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].k + off + c8 * 8);
+          vraw = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].v + off + c8 * 8);
+        }
+        *(u32x4*)(Ks + r * T::RS + c8 * 8) = kraw;
+        *(u32x4*)(Vs + r * T::RS + c8 * 8) = vraw;
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, kraw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) KTs[(c8 * 8 + e) * T::TS + r] = kv[e];
+      }
+    }
+    if (tid < kRows) kps[tid] = (j0 + tid < p.Lk) ? p.kpos[j0 + tid] : kPosMax;
+    __syncthreads();
+
+    // S^T = K Q^T and dP^T = V dO^T: lane holds query lane % 32 and keys out_row(r)
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Ks, lane, st), qf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Vs, lane, st), gf[st], dp, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool vis = kps[out_row(r, lane)] <= qp;
+      const float pr = vis ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2) : 0.f;
+      dp[r] = pr * (dp[r] - del);
+    }
+    // dQ^T += K^T dS^T (scale applied at the end)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const bf16x8 df = to_bf16x8(dp, tt);
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(KTs, lane, db, tt), df, dqT[db], 0, 0, 0);
+    }
+  }
+
+  if (qvalid) {
+    float* dqr = p.dq + row * p.d;
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int col = db * 32 + 8 * k + 4 * h;
+        if (col < p.d) {
+          const f32x4 v = {dqT[db][4 * k] * p.scale, dqT[db][4 * k + 1] * p.scale, dqT[db][4 * k + 2] * p.scale,
+                           dqT[db][4 * k + 3] * p.scale};
+          *(f32x4*)(dqr + col) = v;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+using namespace ra_host;
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t chunks, qpos, kpos, qblk, ktile, table_end, delta, total;
+};
+
+BwdLayout bwd_layout(int batch, int q_heads, int64_t q_len, int64_t total_keys, int n_chunks) {
+  BwdLayout L;
+  const int64_t nqb = (q_len + kRows - 1) / kRows, nkt = (total_keys + kRows - 1) / kRows;
+  L.chunks = 0;
+  L.qpos = L.chunks + al256(sizeof(BwdChunk) * (size_t)(n_chunks > 0 ? n_chunks : 1));
+  L.kpos = L.qpos + al256(sizeof(int) * (size_t)(q_len > 0 ? q_len : 1));
+  L.qblk = L.kpos + al256(sizeof(int) * (size_t)(total_keys > 0 ? total_keys : 1));
+  L.ktile = L.qblk + al256(sizeof(int) * (size_t)(nqb > 0 ? nqb : 1));
+  L.table_end = L.ktile + al256(sizeof(int) * (size_t)(nkt > 0 ? nkt : 1));
+  L.delta = L.table_end;
+  L.total = L.delta + al256(sizeof(float) * (size_t)(batch > 0 ? batch : 0) * (size_t)(q_heads > 0 ? q_heads : 0) *
+                            (size_t)(q_len > 0 ? q_len : 0));
+  return L;
+}
+
+template <int DP>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
+  const int64_t n_kt = (p.Lk + kGroupRows - 1) / kGroupRows;
+  const int64_t n_qt = (p.Lq + kGroupRows - 1) / kGroupRows;
+  timer_begin(s);
+  if (n_kt > 0)
+    hipLaunchKernelGGL((dkdv_kernel<DP>), dim3((unsigned)(n_kt * p.B * p.Hkv)), dim3(kBwdThreads), 0, s, p);
+  timer_end(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  timer_begin(s);
+  hipLaunchKernelGGL((dq_kernel<DP>), dim3((unsigned)(n_qt * p.B * p.Hq)), dim3(kBwdThreads), 0, s, p);
+  timer_end(s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int64_t q_len, int64_t total_keys, int n_chunks) {
+  if (n_chunks < 0) n_chunks = 0;
+  if (q_len < 0) q_len = 0;
+  if (total_keys < 0) total_keys = 0;
+  return bwd_layout(batch, q_heads, q_len, total_keys, n_chunks).total;
+}
+
+int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
+                               const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks,
+                               int n_chunks, int causal, float scale, const float* out, const float* lse,
+                               const void* dout, void* workspace, size_t workspace_bytes, float* dq, float* dk,
+                               float* dv, void* stream) {
+  g_err[0] = 0;
+  int st = check_dims(dtype, batch, q_heads, kv_heads, head_dim);
+  if (st) return st;
+  if (dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs");
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "the backward pass takes head_dim 32, 64 or 128 (got %d)", head_dim);
+  if (n_q_segments < 1 || !q_segments) return fail(RA_ERR_NULL, "at least one query segment is required");
+  if (n_chunks < 0 || (n_chunks > 0 && !chunks)) return fail(RA_ERR_NULL, "chunk array missing");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(RA_ERR_SHAPE, "scale must be finite and > 0");
+  int64_t lq = 0;
+  for (int s = 0; s < n_q_segments; ++s) {
+    const ra_q_segment& g = q_segments[s];
+    if (g.len < 0) return fail(RA_ERR_SHAPE, "query segment %d: negative length", s);
+    if (g.pos_stride < 0) return fail(RA_ERR_SHAPE, "query segment %d: negative pos_stride", s);
+    if (causal && g.len > 0 && !positions_fit(g.global_offset, g.len, pos_step(g.pos_stride)))
+      return fail(RA_ERR_SHAPE, "query segment %d: positions outside [0, 2^31-1)", s);
+    lq += g.len;
+  }
+  int64_t lk = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    if ((st = check_chunk(chunks[c], c, head_dim))) return st;
+    if (chunks[c].len > 0 && !chunk_vec_ok(chunks[c], head_dim, 2))
+      return fail(RA_ERR_UNSUPPORTED, "chunk %d: rows must be 16-byte aligned for the backward pass", c);
+    lk += chunks[c].len;
+  }
+  if (lk > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "more than 2^31-2 keys in total");
+  if (lq == 0 || batch == 0) return RA_OK;
+  if (!q || !out || !lse || !dout || !dq) return fail(RA_ERR_NULL, "q, out, lse, dout and dq must be non-null");
+  if (lk > 0 && (!dk || !dv)) return fail(RA_ERR_NULL, "dk and dv must be non-null");
+  if (!vec_ok(q, head_dim, head_dim, 2) || !vec_ok(dout, head_dim, head_dim, 2) || (uintptr_t)out % 16 != 0 ||
+      (uintptr_t)dq % 16 != 0 || (lk > 0 && ((uintptr_t)dk % 16 != 0 || (uintptr_t)dv % 16 != 0)))
+    return fail(RA_ERR_UNSUPPORTED, "q, dout, out, dq, dk and dv must be 16-byte aligned");
+  const int64_t blocks_q = ((lq + kGroupRows - 1) / kGroupRows) * batch * q_heads;
+  const int64_t blocks_k = ((lk + kGroupRows - 1) / kGroupRows) * batch * kv_heads;
+  if (blocks_q > 0x7fffffffLL || blocks_k > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
+  const BwdLayout L = bwd_layout(batch, q_heads, lq, lk, n_chunks);
+  if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0)
+    return fail(RA_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
+                workspace_bytes);
+
+  // host tables: chunk descriptors, query and key positions, per-block bounds
+  char* host = (char*)calloc(1, L.table_end);
+  if (!host) return fail(RA_ERR_UNSUPPORTED, "host allocation failed");
+  BwdChunk* hc = (BwdChunk*)(host + L.chunks);
+  int* hqp = (int*)(host + L.qpos);
+  int* hkp = (int*)(host + L.kpos);
+  int* hqb = (int*)(host + L.qblk);
+  int* hkt = (int*)(host + L.ktile);
+  int nc = 0;
+  int64_t start = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    const ra_kv_chunk& ch = chunks[c];
+    if (ch.len == 0) continue;
+    BwdChunk& d = hc[nc++];
+    d.k = ch.k;
+    d.v = ch.v;
+    d.start = start;
+    d.len = ch.len;
+    d.sb = ch.stride_b;
+    d.sh = ch.stride_h;
+    d.ss = ch.stride_s;
+    d.pos0 = (int32_t)ch.global_offset;
+    d.ps = (int32_t)pos_step(ch.pos_stride);
+    for (int64_t i = 0; i < ch.len; ++i) hkp[start + i] = causal ? (int)(ch.global_offset + d.ps * i) : 0;
+    start += ch.len;
+  }
+  int64_t row = 0;
+  for (int s = 0; s < n_q_segments; ++s) {
+    const ra_q_segment& g = q_segments[s];
+    for (int64_t i = 0; i < g.len; ++i)
+      hqp[row + i] = causal ? (int)(g.global_offset + pos_step(g.pos_stride) * i) : kPosAllQ;
+    row += g.len;
+  }
+  for (int64_t qb = 0; qb * kRows < lq; ++qb) {
+    int mx = kPosMinQ;
+    for (int64_t i = qb * kRows; i < lq && i < (qb + 1) * kRows; ++i) mx = hqp[i] > mx ? hqp[i] : mx;
+    hqb[qb] = mx;
+  }
+  for (int64_t t = 0; t * kRows < lk; ++t) {
+    int mn = kPosMax;
+    for (int64_t j = t * kRows; j < lk && j < (t + 1) * kRows; ++j) mn = hkp[j] < mn ? hkp[j] : mn;
+    hkt[t] = mn;
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(workspace, host, L.table_end, hipMemcpyHostToDevice, hs);
+  free(host);
+  if (e != hipSuccess) return hip_fail(e, "ring_attention_backward table copy");
+
+  BwdParams p = {};
+  char* ws = (char*)workspace;
+  p.q = (const __bf16*)q;
+  p.dout = (const __bf16*)dout;
+  p.out = out;
+  p.lse = lse;
+  p.delta = (float*)(ws + L.delta);
+  p.qpos = (const int*)(ws + L.qpos);
+  p.kpos = (const int*)(ws + L.kpos);
+  p.qblk_max = (const int*)(ws + L.qblk);
+  p.ktile_min = (const int*)(ws + L.ktile);
+  p.chunks = (const BwdChunk*)(ws + L.chunks);
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.Lq = lq;
+  p.Lk = lk;
+  p.n_chunks = nc > 0 ? nc : 1;
+  p.B = batch;
+  p.Hq = q_heads;
+  p.Hkv = kv_heads;
+  p.d = head_dim;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.c2 = scale * kLog2e;
+
+  const int64_t rows = (int64_t)batch * q_heads * lq;
+  int lpr = 1, sh = 0;
+  while (lpr < head_dim / 8) {
+    lpr <<= 1;
+    ++sh;
+  }
+  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((rows * lpr + 255) / 256)), dim3(256), 0, hs, rows, head_dim,
+                     lpr, sh, (const __bf16*)dout, out, p.delta);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "ring_attention_backward delta launch");
+  if (head_dim == 32)
+    e = launch_bwd<32>(p, hs);
+  else if (head_dim == 64)
+    e = launch_bwd<64>(p, hs);
+  else
+    e = launch_bwd<128>(p, hs);
+  if (e != hipSuccess) return hip_fail(e, "ring_attention_backward launch");
+  return RA_OK;
+}
+
+}  // extern "C"

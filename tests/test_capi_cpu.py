@@ -142,3 +142,21 @@ def test_python_layer_refuses_cpu_tensors():
 def test_kernel_timer_read_rejects_null(lib):
     # host-side check only: no event is created or read
     assert lib.ra_kernel_timer_read(None, None) == 1
+
+
+def test_backward_validation_codes(lib):
+    seg = (api.QSegment * 1)(api.QSegment(4, 0))
+    ch = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 8, 0, 2 * 8 * 64, 8 * 64, 64))
+
+    def bwd(dtype=1, d=64, Hq=2, Hkv=2, ws=None, wsb=0, dq=FAKE):
+        return lib.ra_ring_attention_backward(dtype, 1, Hq, Hkv, d, FAKE, seg, 1, ch, 1, 0, 0.125, FAKE, FAKE, FAKE,
+                                              ws, wsb, dq, FAKE, FAKE, None)
+
+    assert bwd(dtype=0) == 4  # fp32: not supported by the backward kernels
+    assert bwd(d=40) == 4
+    assert bwd(Hq=3) == 2
+    assert bwd(dq=None) == 1
+    assert bwd() == 6  # no workspace
+    assert b"workspace" in lib.ra_last_error()
+    need = lib.ra_ring_backward_workspace_bytes(1, 2, 4, 8, 1)
+    assert need % 256 == 0 and need >= 4 * (4 + 8) + 4 * 2 * 4

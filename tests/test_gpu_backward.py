@@ -1,0 +1,126 @@
+"""Parity of the HIP backward pass with the fp64 gradient oracle (needs an MI355X).
+
+Every call goes through the C ABI. The oracle differentiates ordinary
+attention over the concatenated chunks from the exact (upcast) bf16 inputs
+("Ring Attention: Distributed Reads with Online Softmax", section "Backward
+must aggregate shared dependencies": check against a single-device reference,
+gradients included).
+
+Tolerance, from the arithmetic: the kernels round the probabilities p and
+the score gradients ds to bf16 (relative error <= 2^-9) before the matrix
+products that form dV, dK and dQ, and sum in fp32. Each output element is a
+sum of terms whose bf16-rounded factors carry independent errors, so its
+error is below 2^-9 times the sum of the terms' magnitudes and, in practice,
+a small fraction of that. The tests bound the error by BWD_MAX times the largest
+reference magnitude and BWD_MEAN times the mean reference magnitude of each gradient.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_chunk_amd as ra
+from ring_attention_chunk_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BWD_MAX, BWD_MEAN = 1e-2, 5e-3
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+CASES = [
+    # name, B, Hq, Hkv, d, q_segments, chunks, causal, position step
+    ("d64_nc_gqa", 2, 4, 2, 64, [(0, 200)], [(0, 100), (100, 37), (137, 150)], False, 1),
+    ("d128_causal", 1, 3, 3, 128, [(200, 260)], [(0, 64), (64, 200), (264, 236)], True, 1),
+    ("d32_zigzag_gqa", 1, 4, 1, 32, [(64, 64), (448, 64)], [(64 * j, 64) for j in (1, 6, 0, 7, 3, 4, 2, 5)],
+     True, 1),
+    ("d64_striped", 1, 2, 2, 64, [(3, 150)], [(j, 150) for j in wl.ring_order(3, 4)], True, 4),
+    ("d128_nc_one_chunk", 1, 2, 1, 128, [(0, 129)], [(0, 257)], False, 1),
+    ("d64_causal_rows_before_keys", 1, 2, 2, 64, [(0, 96)], [(50, 100)], True, 1),
+]
+
+
+def _run_case(w):
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    g = torch.Generator().manual_seed(zlib.crc32(w.name.encode()))
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    out, lse = ra.ring_attention(q, kc, vc, w.q_runs, w.kv_offsets, causal=w.causal, return_lse=True,
+                                 kv_position_strides=w.kv_strides)
+    dq, dks, dvs = ra.ring_attention_backward(q, kc, vc, out, lse, dout, w.q_runs, w.kv_offsets, causal=w.causal,
+                                              kv_position_strides=w.kv_strides)
+    torch.cuda.synchronize()
+    return q, kc, vc, dout, out, lse, dq, dks, dvs
+
+
+def _compare(name, got, ref):
+    err = np.abs(got - ref)
+    scale_max = max(np.abs(ref).max(), 1e-30)
+    scale_mean = max(np.abs(ref).mean(), 1e-30)
+    print(f"  {name}: max err {err.max():.3e} (ref max {scale_max:.3e}), mean err {err.mean():.3e} "
+          f"(ref mean {scale_mean:.3e})", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err.max() <= BWD_MAX * scale_max, (name, err.max(), scale_max)
+    assert err.mean() <= BWD_MEAN * scale_mean, (name, err.mean(), scale_mean)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_small_shares(case):
+    name, B, Hq, Hkv, d, qs, ch, causal, step = case
+    _say(f"backward {name}")
+    w = wl.custom(name, "bf16", B, Hq, Hkv, d, qs, ch, causal, seed=zlib.crc32(name.encode()) % 1000,
+                  pos_stride=step)
+    q, kc, vc, dout, out, lse, dq, dks, dvs = _run_case(w)
+    ref = oracle.attention_backward(q.cpu(), [c.cpu() for c in kc], [c.cpu() for c in vc], dout.cpu(),
+                                    wl.q_positions(w), w.kv_offsets, causal=causal, kv_strides=w.kv_strides)
+    _compare("dq", _np(dq), ref["dq"])
+    _compare("dk", np.concatenate([_np(t) for t in dks], axis=2), ref["dk"])
+    _compare("dv", np.concatenate([_np(t) for t in dvs], axis=2), ref["dv"])
+    # keys that no local query sees get exact zeros
+    if causal:
+        kpos = wl.k_positions(w)
+        unseen = kpos > wl.q_positions(w).max()
+        if unseen.any():
+            assert torch.all(torch.cat(dks, 2)[:, :, torch.from_numpy(unseen)] == 0)
+
+
+def test_backward_is_bit_reproducible_and_split_invariant_in_dq():
+    w = wl.custom("bwd_rep", "bf16", 1, 2, 2, 64, [(100, 200)], [(0, 128), (128, 128), (256, 128)], True, seed=3)
+    _say("backward repeat and re-split")
+    q, kc, vc, dout, out, lse, dq, dks, dvs = _run_case(w)
+    dq2, dks2, dvs2 = ra.ring_attention_backward(q, kc, vc, out, lse, dout, w.q_runs, w.kv_offsets, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2)
+    assert all(torch.equal(a, b) for a, b in zip(dks, dks2))
+    assert all(torch.equal(a, b) for a, b in zip(dvs, dvs2))
+    # the same ordered keys cut elsewhere: identical per-key gradients (every key row is summed over the
+    # same queries in the same order) and identical dq (key tiles depend only on the list order)
+    r = wl.resplit(w, [50, 200, 300])
+    _, k, v, _, _ = wl.generate_torch(w, DEV)
+    kc2, vc2 = wl.chunk_views(r, k, v)
+    dq3, dks3, dvs3 = ra.ring_attention_backward(q, kc2, vc2, out, lse, dout, r.q_runs, r.kv_offsets, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq3)
+    assert torch.equal(torch.cat(dks, 2), torch.cat(dks3, 2))
+    assert torch.equal(torch.cat(dvs, 2), torch.cat(dvs3, 2))
+
+
+def test_backward_errors_raise():
+    _say("backward errors")
+    q = torch.randn(1, 2, 8, 40, device=DEV).to(torch.bfloat16)
+    out = torch.zeros(1, 2, 8, 40, device=DEV)
+    lse = torch.zeros(1, 2, 8, device=DEV)
+    with pytest.raises(ra.RingAttentionError):  # head_dim 40 is not supported by the backward kernels
+        ra.ring_attention_backward(q, [q], [q], out, lse, q)
+    qf = torch.randn(1, 2, 8, 64, device=DEV)
+    with pytest.raises(ra.RingAttentionError):  # fp32 inputs
+        ra.ring_attention_backward(qf, [qf], [qf], qf, lse, qf)
