@@ -109,6 +109,39 @@ def timed_with_kernel(fn, steps, warmup, torch, api):
     return start.elapsed_time(stop) / steps, total / n
 
 
+def backward_leg(w, q, kc, vc, offs, args, torch, ra):
+    """The backward pass of the same share (dQ, and this share's dK, dV per chunk) from the forward's out
+    and lse, with a seeded bf16 upstream gradient. Counted flops: 10*d per allowed pair and query head
+    (five matrix products of 2*d: S, dP, dV, dK, dQ); the kernels recompute S and dP a second time."""
+    from ring_attention_chunk_amd import workloads as wl
+
+    dev = q.device
+    out, lse = ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
+                                 return_lse=True, kv_position_strides=w.kv_strides)
+    g = torch.Generator(device=dev).manual_seed(7)
+    dout = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
+    ws = torch.empty(ra.api.backward_workspace_bytes(tuple(q.shape), [c.shape[2] for c in kc]), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        return ra.ring_attention_backward(q, kc, vc, out, lse, dout, w.q_runs, offs, causal=w.causal,
+                                          scale=w.softmax_scale, kv_position_strides=w.kv_strides, workspace=ws)
+
+    steps = max(5, min(args.steps, 20))
+    ms, pair_ms = timed_with_kernel(step, steps, 3, torch, ra.api)
+    kernels_ms = 2 * pair_ms  # the dK/dV kernel and the dQ kernel, each timed by its own event pair
+    flops = 10 * w.head_dim * w.q_heads * w.batch * wl.unmasked_pairs_per_head(w)
+    return {
+        "ms": round(ms, 4),
+        "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+        "kernels_ms": round(kernels_ms, 4),
+        "kernels_TFLOP/s": round(flops / (kernels_ms * 1e-3) / 1e12, 2),
+        "frac_of_bf16_peak": round(flops / (kernels_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "counted_flops": flops,
+        "shape": f"{w.name}: dq, and dk, dv of every chunk; bf16 dout",
+    }
+
+
 def dominant_kernel(w):
     """Name of the kernel that does a workload's attention: every bf16 workload here (aligned rows,
     whole 16-byte pieces) runs the pipelined bf16 kernel, fp32 the general one."""
@@ -420,6 +453,8 @@ def main():
             "shape": f"{rows} rows x d={d}, fp32, 4 rotating buffer sets",
         }
         del sets, src, dst, srcs
+        if w.dtype == "bf16" and w.head_dim in (32, 64, 128):
+            legs["ring_attention_backward"] = backward_leg(w, q, kc, vc, offs, args, torch, ra)
         result["legs"] = legs
 
     if not args.no_cpu_baseline:

@@ -39,13 +39,15 @@ from .direct import _f64, key_positions
 
 
 def attention_backward(q, key_chunks, value_chunks, dout, q_positions=None, kv_offsets=None, causal=False,
-                       scale=None, kv_strides=None):
+                       scale=None, kv_strides=None, max_block_elems=1 << 24):
     """Gradients of ``out = attention(q, chunks)`` against ``dout``.
 
     q, dout [B, Hq, Lq, d]; chunks [B, Hkv, len, d]. Returns a dict with
     ``dq`` [B, Hq, Lq, d] and ``dk``, ``dv`` [B, Hkv, Lk, d] over the
     concatenated key list (chunk ``c`` is the slice of its keys), plus the
-    forward ``out`` and ``lse`` it recomputed.
+    forward ``out`` and ``lse`` it recomputed. Query rows are taken a block at
+    a time (at most ``max_block_elems`` scores) only to bound memory; the key
+    gradients add the blocks' contributions.
     """
     q = _f64(q)
     do = _f64(dout)
@@ -56,32 +58,33 @@ def attention_backward(q, key_chunks, value_chunks, dout, q_positions=None, kv_o
     group = Hq // Hkv
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    if causal:
-        qpos = np.asarray(q_positions, dtype=np.int64)
-        kpos = key_positions([c.shape[2] for c in key_chunks], kv_offsets, kv_strides)
-        allowed = kpos[None, :] <= qpos[:, None]
-    else:
-        allowed = np.ones((Lq, n), dtype=bool)
+    qpos = np.asarray(q_positions, dtype=np.int64) if causal else None
+    kpos = key_positions([c.shape[2] for c in key_chunks], kv_offsets, kv_strides) if causal else None
     dq = np.zeros_like(q)
     dk = np.zeros((B, Hkv, n, d))
     dv = np.zeros((B, Hkv, n, d))
     out = np.zeros((B, Hq, Lq, d))
     lse = np.full((B, Hq, Lq), -np.inf)
+    rb = max(1, min(Lq, max_block_elems // max(n, 1))) if Lq else 1
     for b in range(B):
         for h in range(Hq):
             hk = h // group
-            s = scale * (q[b, h] @ k[b, hk].T)
-            s = np.where(allowed, s, -np.inf)
-            m = s.max(axis=1) if n else np.full(Lq, -np.inf)
-            seen = ~np.isneginf(m)
-            w = np.exp(s - np.where(seen, m, 0.0)[:, None])
-            l = w.sum(axis=1)
-            p = np.where(seen[:, None], w / np.where(seen, l, 1.0)[:, None], 0.0)
-            out[b, h] = p @ v[b, hk]
-            lse[b, h] = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
-            dp = do[b, h] @ v[b, hk].T
-            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-            dq[b, h] = scale * (ds @ k[b, hk])
-            dk[b, hk] += scale * (ds.T @ q[b, h])
-            dv[b, hk] += p.T @ do[b, h]
+            for r0 in range(0, Lq, rb):
+                r1 = min(Lq, r0 + rb)
+                s = scale * (q[b, h, r0:r1] @ k[b, hk].T)
+                if causal:
+                    s = np.where(kpos[None, :] <= qpos[r0:r1, None], s, -np.inf)
+                m = s.max(axis=1) if n else np.full(r1 - r0, -np.inf)
+                seen = ~np.isneginf(m)
+                w = np.exp(s - np.where(seen, m, 0.0)[:, None])
+                l = w.sum(axis=1)
+                p = np.where(seen[:, None], w / np.where(seen, l, 1.0)[:, None], 0.0)
+                out[b, h, r0:r1] = p @ v[b, hk]
+                lse[b, h, r0:r1] = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
+                g = do[b, h, r0:r1]
+                dp = g @ v[b, hk].T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h, r0:r1] = scale * (ds @ k[b, hk])
+                dk[b, hk] += scale * (ds.T @ q[b, h, r0:r1])
+                dv[b, hk] += p.T @ g
     return {"dq": dq, "dk": dk, "dv": dv, "out": out, "lse": lse}

@@ -234,6 +234,12 @@ def workspace_bytes(query_shape, key_lengths, n_q_segments: int = 1) -> int:
                                                       n_q_segments))
 
 
+def backward_workspace_bytes(query_shape, key_lengths) -> int:
+    """Bytes of device workspace ``ring_attention_backward`` needs for this shape."""
+    B, Hq, Lq, _ = query_shape
+    return int(load_library().ra_ring_backward_workspace_bytes(B, Hq, Lq, int(sum(key_lengths)), len(key_lengths)))
+
+
 def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global_offset: QOffset = 0,
                    kv_global_offsets: Optional[Sequence[int]] = None, causal: bool = False,
                    scale: Optional[float] = None, return_lse: bool = False, workspace=None,

@@ -124,3 +124,32 @@ def test_backward_errors_raise():
     qf = torch.randn(1, 2, 8, 64, device=DEV)
     with pytest.raises(ra.RingAttentionError):  # fp32 inputs
         ra.ring_attention_backward(qf, [qf], [qf], qf, lse, qf)
+
+
+@pytest.mark.parametrize("i", [1, 2])
+def test_backward_full_size(i):
+    """A full-size share in the benchmark's launch configuration: head 0 in full against the oracle,
+    and on every head the sums that hold at any size: the key gradients of a head sum to zero (each row
+    of ds sums to zero) and its value gradients sum to the upstream gradients of the rows that see a key
+    (each row's weights sum to one)."""
+    w = wl.config(i)
+    _say(f"backward full size {w.name}")
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    g = torch.Generator(device=DEV).manual_seed(7)
+    dout = torch.randn(q.shape, device=DEV, generator=g).to(torch.bfloat16)
+    out, lse = ra.ring_attention(q, kc, vc, w.q_runs, w.kv_offsets, causal=w.causal, return_lse=True)
+    dq, dks, dvs = ra.ring_attention_backward(q, kc, vc, out, lse, dout, w.q_runs, w.kv_offsets, causal=w.causal)
+    torch.cuda.synchronize()
+    dk, dv = torch.cat(dks, 2), torch.cat(dvs, 2)
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    group = w.q_heads // w.kv_heads
+    seen = torch.isfinite(lse)  # rows that see at least one key
+    do_seen = (dout.float() * seen[..., None]).reshape(w.batch, w.kv_heads, group, w.lq, w.head_dim)
+    sum_do = do_seen.sum(dim=(2, 3))
+    assert ((dv.sum(2) - sum_do).abs() <= 1e-2 * do_seen.abs().sum(dim=(2, 3))).all()
+    assert (dk.sum(2).abs() <= 1e-2 * dk.abs().sum(2)).all()
+    ref = oracle.attention_backward(q[:, :1].cpu(), [c[:, :1].cpu() for c in kc], [c[:, :1].cpu() for c in vc],
+                                    dout[:, :1].cpu(), wl.q_positions(w), w.kv_offsets, causal=w.causal)
+    _compare("dq head 0", _np(dq[:, :1]), ref["dq"])
+    _compare("dk head 0", _np(dk[:, :1]), ref["dk"])
+    _compare("dv head 0", _np(dv[:, :1]), ref["dv"])
