@@ -18,11 +18,12 @@
 //  * dkdv_kernel: a workgroup owns 128 keys of one (batch, kv head), 32 per
 //    wave, and walks every query row of every query head of its group in
 //    blocks of 32. K and V stay in registers as MFMA B operands; each query
-//    block (Q, dO, their transposes, lse, delta, positions) is staged once in
-//    LDS for the four waves. S = Q K^T and dP = dO V^T put one key per lane and
-//    16 queries in its registers; those registers, rounded to bf16, are
-//    directly the B operand of dV^T += dO^T P and dK^T += Q^T dS, whose A
-//    operands read the transposed tiles in the same (permuted) query order.
+//    block (Q, dO, lse, delta, positions) is staged once in LDS for the four
+//    waves, its global loads issued one block ahead. S = Q K^T and dP = dO V^T
+//    put one key per lane and 16 queries in its registers; those registers,
+//    rounded to bf16, are directly the B operand of dV^T += dO^T P and
+//    dK^T += Q^T dS, whose A operands are read transposed from the row-major
+//    tiles (ds_read_b64_tr_b16) in the same (permuted) query order.
 //  * dq_kernel: a workgroup owns 128 query rows of one (batch, head), 32 per
 //    wave, and walks the keys in tiles of 32. Q and dO stay in registers;
 //    S^T = K Q^T and dP^T = V dO^T put one query per lane; dQ^T += K^T dS^T.
@@ -129,42 +130,53 @@ __global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int d, int lpr
 }
 
 // ---------------------------------------------------------------------------
-// Staging of a 32-row block of a [rows, d] bf16 tensor into LDS, row-major
-// (row stride DP + 8 elements) and transposed (row stride 32 + 4 elements).
-// Rows at or past `nrows` and columns past d are zero.
+// 32-row blocks of a [rows, d] bf16 tensor in LDS, row-major with a row stride
+// of DP + 16 elements: a transposing read then touches 16 distinct bank pairs
+// per 16 lanes. Blocks go HBM -> registers (issued one block ahead, so the
+// loads run under the current block's matrix work) -> LDS.
 
 template <int DP>
 struct Tile {
-  static constexpr int RS = DP + 8;       // row-major stride (elements)
-  static constexpr int TS = kRows + 4;    // transposed stride (elements)
-  static constexpr int PIECES = kRows * DP / 8;
+  static constexpr int RS = DP + 16;                     // row stride (elements)
+  static constexpr int PIECES = kRows * DP / 8;          // 16-byte pieces per block
+  static constexpr int PER = (PIECES + kBwdThreads - 1) / kBwdThreads;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
 
-  static __device__ __forceinline__ void stage(const __bf16* src, int64_t nrows, int d, __bf16* rm, __bf16* tr,
-                                               int tid) {
-    for (int pc = tid; pc < PIECES; pc += kBwdThreads) {
-      const int r = pc / (DP / 8), c8 = pc % (DP / 8);
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (r < nrows && c8 * 8 < d) raw = *(const u32x4*)(src + (int64_t)r * d + c8 * 8);
-      *(u32x4*)(rm + r * RS + c8 * 8) = raw;
-      const bf16x8 v = __builtin_bit_cast(bf16x8, raw);
+  // piece k of this thread: row and 8-column group; false past the block
+  static __device__ __forceinline__ bool piece(int tid, int k, int& r, int& c8) {
+    const int pc = tid + k * kBwdThreads;
+    r = pc / (DP / 8);
+    c8 = pc % (DP / 8);
+    return PIECES % kBwdThreads == 0 || pc < PIECES;
+  }
+
+  static __device__ __forceinline__ void put(__bf16* rm, int tid, const u32x4* regs) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) tr[(c8 * 8 + i) * TS + r] = v[i];
+    for (int k = 0; k < PER; ++k) {
+      int r, c8;
+      if (piece(tid, k, r, c8)) *(u32x4*)(rm + r * RS + c8 * 8) = regs[k];
     }
   }
 
-  // A operand of a 32x32x16 MFMA from the row-major tile: row lane % 32, k = 16 s + 8 h .. +7.
+  // A operand of a 32x32x16 MFMA: row lane % 32 of the block, k = 16 s + 8 h .. +7.
   static __device__ __forceinline__ bf16x8 rows_frag(const __bf16* rm, int lane, int s) {
     return *(const bf16x8*)(rm + (lane & 31) * RS + 16 * s + 8 * (lane >> 5));
   }
 
-  // A operand from the transposed tile: row db * 32 + lane % 32 (a column of the block), and the
-  // k slots in the order of an MFMA output's registers 8t .. 8t+7: rows 16t + 4h .. +3 and
-  // 16t + 8 + 4h .. +3 of the block.
-  static __device__ __forceinline__ bf16x8 cols_frag(const __bf16* tr, int lane, int db, int t) {
-    const __bf16* row = tr + (db * 32 + (lane & 31)) * TS + 16 * t + 4 * (lane >> 5);
-    const bf16x4 a = *(const bf16x4*)row;
-    const bf16x4 b = *(const bf16x4*)(row + 8);
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  // A operand holding the block transposed: row db * 32 + lane % 32 of the transpose (a column of
+  // the block), and k slots in the order of an MFMA output's registers 8t .. 8t+7, i.e. block rows
+  // 16t + 4h .. +3, then 16t + 8 + 4h .. +3. Each half is one ds_read_b64_tr_b16: lane j of a
+  // 16-lane group addresses block row base + j / 4, columns c0 + 4 (j % 4) .. +3, and lane i of the
+  // group receives column c0 + i of block rows base .. base + 3.
+  static __device__ __forceinline__ bf16x8 cols_frag(const __bf16* rm, int lane, int db, int t) {
+    const int j = lane & 15;
+    const int base = 16 * t + 4 * (lane >> 5) + (j >> 2);
+    const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+    const __bf16* a = rm + base * RS + col;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)a);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a + 8 * RS));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
 
@@ -179,10 +191,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   using T = Tile<DP>;
   constexpr int NS = DP / 16;  // k-steps over head_dim
   constexpr int NB = DP / 32;  // 32-row blocks of head_dim
+  constexpr int PER = T::PER;
   __shared__ __attribute__((aligned(16))) __bf16 Qs[kRows * T::RS];
-  __shared__ __attribute__((aligned(16))) __bf16 QTs[DP * T::TS];
   __shared__ __attribute__((aligned(16))) __bf16 Gs[kRows * T::RS];
-  __shared__ __attribute__((aligned(16))) __bf16 GTs[DP * T::TS];
   __shared__ float lse2s[kRows], dels[kRows];
   __shared__ int qps[kRows];
   __shared__ int kmin_red[kBwdWaves];
@@ -232,51 +243,82 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
     dvT[i] = f32x16{};
   }
 
+  // walk (query head of the group, 32-row block) in order, skipping blocks that see none of our keys
   const int n_qb = (int)((p.Lq + kRows - 1) / kRows);
-  for (int g = 0; g < group; ++g) {
-    const int hq = hk * group + g;
-    const int64_t rowbase = ((int64_t)b * p.Hq + hq) * p.Lq;
-    for (int qb = 0; qb < n_qb; ++qb) {
-      if (p.causal && p.qblk_max[qb] < kmin) continue;  // uniform
-      const int64_t r0 = (int64_t)qb * kRows;
-      const int64_t nrows = min((int64_t)kRows, p.Lq - r0);
-      __syncthreads();  // previous block's LDS reads are done
-      T::stage(p.q + (rowbase + r0) * p.d, nrows, p.d, Qs, QTs, tid);
-      T::stage(p.dout + (rowbase + r0) * p.d, nrows, p.d, Gs, GTs, tid);
-      if (tid < kRows) {
-        const bool v = tid < nrows;
-        const float ls = v ? p.lse[rowbase + r0 + tid] : 0.f;
-        lse2s[tid] = (ls == -INFINITY) ? 0.f : ls * kLog2e;
-        dels[tid] = v ? p.delta[rowbase + r0 + tid] : 0.f;
-        qps[tid] = v ? p.qpos[r0 + tid] : kPosMinQ;
+  auto advance = [&](int& g, int& qb) {
+    while (true) {
+      if (++qb >= n_qb) {
+        qb = 0;
+        if (++g >= group) return false;
       }
-      __syncthreads();
+      if (!p.causal || p.qblk_max[qb] >= kmin) return true;
+    }
+  };
+  u32x4 pq[PER], pg[PER];
+  float pl = 0.f, pd = 0.f;
+  int pp = kPosMinQ;
+  auto fetch = [&](int g, int qb) {
+    const int64_t rowbase = ((int64_t)b * p.Hq + hk * group + g) * p.Lq;
+    const int64_t r0 = (int64_t)qb * kRows;
+    const int64_t nrows = min((int64_t)kRows, p.Lq - r0);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      int r, c8;
+      pq[k] = u32x4{0u, 0u, 0u, 0u};
+      pg[k] = u32x4{0u, 0u, 0u, 0u};
+      if (T::piece(tid, k, r, c8) && r < nrows) {
+        pq[k] = *(const u32x4*)(p.q + (rowbase + r0 + r) * p.d + c8 * 8);
+        pg[k] = *(const u32x4*)(p.dout + (rowbase + r0 + r) * p.d + c8 * 8);
+      }
+    }
+    if (tid < kRows) {
+      const bool v = tid < nrows;
+      pl = v ? p.lse[rowbase + r0 + tid] : 0.f;
+      pd = v ? p.delta[rowbase + r0 + tid] : 0.f;
+      pp = v ? p.qpos[r0 + tid] : kPosMinQ;
+    }
+  };
 
-      // S = Q K^T and dP = dO V^T: lane holds key lane % 32 and queries out_row(r)
-      f32x16 s = f32x16{}, dp = f32x16{};
+  int cg = 0, cqb = -1;
+  bool have = advance(cg, cqb);
+  if (have) fetch(cg, cqb);
+  while (have) {
+    __syncthreads();  // the previous block's LDS reads are done
+    T::put(Qs, tid, pq);
+    T::put(Gs, tid, pg);
+    if (tid < kRows) {
+      lse2s[tid] = (pl == -INFINITY) ? 0.f : pl * kLog2e;
+      dels[tid] = pd;
+      qps[tid] = pp;
+    }
+    __syncthreads();
+    have = advance(cg, cqb);
+    if (have) fetch(cg, cqb);  // in flight during the matrix work below
+
+    // S = Q K^T and dP = dO V^T: lane holds key lane % 32 and queries out_row(r)
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Qs, lane, st), kf[st], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Gs, lane, st), vf[st], dp, 0, 0, 0);
-      }
+    for (int st = 0; st < NS; ++st) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Qs, lane, st), kf[st], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Gs, lane, st), vf[st], dp, 0, 0, 0);
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = out_row(r, lane);
-        const bool vis = kp <= qps[qi];
-        const float pr = vis ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2s[qi]) : 0.f;
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - dels[qi]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
+    for (int r = 0; r < 16; ++r) {
+      const int qi = out_row(r, lane);
+      const bool vis = kp <= qps[qi];
+      const float pr = vis ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2s[qi]) : 0.f;
+      s[r] = pr;
+      dp[r] = pr * (dp[r] - dels[qi]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 pf = to_bf16x8(s, t);
-        const bf16x8 df = to_bf16x8(dp, t);
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 pf = to_bf16x8(s, t);
+      const bf16x8 df = to_bf16x8(dp, t);
 #pragma unroll
-        for (int db = 0; db < NB; ++db) {
-          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(GTs, lane, db, t), pf, dvT[db], 0, 0, 0);
-          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(QTs, lane, db, t), df, dkT[db], 0, 0, 0);
-        }
+      for (int db = 0; db < NB; ++db) {
+        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(Gs, lane, db, t), pf, dvT[db], 0, 0, 0);
+        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(Qs, lane, db, t), df, dkT[db], 0, 0, 0);
       }
     }
   }
@@ -309,8 +351,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   using T = Tile<DP>;
   constexpr int NS = DP / 16;
   constexpr int NB = DP / 32;
+  constexpr int PER = T::PER;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kRows * T::RS];
-  __shared__ __attribute__((aligned(16))) __bf16 KTs[DP * T::TS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[kRows * T::RS];
   __shared__ int kps[kRows];
   __shared__ int qmax_red[kBwdWaves];
@@ -353,38 +395,46 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NB; ++db) dqT[db] = f32x16{};
 
+  // key tiles of 32 in list order, skipping tiles after every query of the workgroup
+  const int n_kt = (int)((p.Lk + kRows - 1) / kRows);
+  auto advance = [&](int& t) {
+    while (++t < n_kt)
+      if (!p.causal || p.ktile_min[t] <= qmax) return true;
+    return false;
+  };
   // staging cursors: each thread's pieces keep their row slot from tile to tile
-  constexpr int PER = (T::PIECES + kBwdThreads - 1) / kBwdThreads;
   int cur[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) cur[k] = 0;
-
-  const int n_kt = (int)((p.Lk + kRows - 1) / kRows);
-  for (int t = 0; t < n_kt; ++t) {
-    if (p.causal && p.ktile_min[t] > qmax) continue;  // uniform
+  u32x4 pk[PER], pv[PER];
+  int pkp = kPosMax;
+  auto fetch = [&](int t) {
     const int64_t j0 = (int64_t)t * kRows;
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int pc = tid + k * kBwdThreads;
-      if (pc < T::PIECES) {
-        const int r = pc / (DP / 8), c8 = pc % (DP / 8);
-        const int64_t j = j0 + r;
-        u32x4 kraw = {0u, 0u, 0u, 0u}, vraw = {0u, 0u, 0u, 0u};
-        if (j < p.Lk && c8 * 8 < p.d) {
-          const int64_t off = key_offset(p, j, b, hk, cur[k]);
-          kraw = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].k + off + c8 * 8);
-          vraw = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].v + off + c8 * 8);
-        }
-        *(u32x4*)(Ks + r * T::RS + c8 * 8) = kraw;
-        *(u32x4*)(Vs + r * T::RS + c8 * 8) = vraw;
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, kraw);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) KTs[(c8 * 8 + e) * T::TS + r] = kv[e];
+      int r, c8;
+      pk[k] = u32x4{0u, 0u, 0u, 0u};
+      pv[k] = u32x4{0u, 0u, 0u, 0u};
+      if (T::piece(tid, k, r, c8) && j0 + r < p.Lk) {
+        const int64_t off = key_offset(p, j0 + r, b, hk, cur[k]);
+        pk[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].k + off + c8 * 8);
+        pv[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].v + off + c8 * 8);
       }
     }
-    if (tid < kRows) kps[tid] = (j0 + tid < p.Lk) ? p.kpos[j0 + tid] : kPosMax;
+    if (tid < kRows) pkp = (j0 + tid < p.Lk) ? p.kpos[j0 + tid] : kPosMax;
+  };
+
+  int t = -1;
+  bool have = advance(t);
+  if (have) fetch(t);
+  while (have) {
     __syncthreads();
+    T::put(Ks, tid, pk);
+    T::put(Vs, tid, pv);
+    if (tid < kRows) kps[tid] = pkp;
+    __syncthreads();
+    have = advance(t);
+    if (have) fetch(t);  // in flight during the matrix work below
 
     // S^T = K Q^T and dP^T = V dO^T: lane holds query lane % 32 and keys out_row(r)
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -405,7 +455,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
       const bf16x8 df = to_bf16x8(dp, tt);
 #pragma unroll
       for (int db = 0; db < NB; ++db)
-        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(KTs, lane, db, tt), df, dqT[db], 0, 0, 0);
+        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(Ks, lane, db, tt), df, dqT[db], 0, 0, 0);
     }
   }
 
