@@ -49,6 +49,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
@@ -194,8 +195,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
   constexpr int PER = T::PER;
   __shared__ __attribute__((aligned(16))) __bf16 Qs[kRows * T::RS];
   __shared__ __attribute__((aligned(16))) __bf16 Gs[kRows * T::RS];
-  __shared__ float lse2s[kRows], dels[kRows];
-  __shared__ int qps[kRows];
+  __shared__ __attribute__((aligned(16))) float lse2s[kRows];
+  __shared__ __attribute__((aligned(16))) float dels[kRows];
+  __shared__ __attribute__((aligned(16))) int qps[kRows];
   __shared__ int kmin_red[kBwdWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
@@ -302,13 +304,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Qs, lane, st), kf[st], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Gs, lane, st), vf[st], dp, 0, 0, 0);
     }
+    // registers 4i .. 4i+3 hold queries 8i + 4h .. +3: one 16-byte LDS read per table and group
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qi = out_row(r, lane);
-      const bool vis = kp <= qps[qi];
-      const float pr = vis ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2s[qi]) : 0.f;
-      s[r] = pr;
-      dp[r] = pr * (dp[r] - dels[qi]);
+    for (int i = 0; i < 4; ++i) {
+      const int q0 = 8 * i + 4 * h;
+      const f32x4 ls = *(const f32x4*)(lse2s + q0);
+      const f32x4 de = *(const f32x4*)(dels + q0);
+      const i32x4 qq = *(const i32x4*)(qps + q0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * i + e;
+        const float pr = (kp <= qq[e]) ? __builtin_amdgcn_exp2f(s[r] * p.c2 - ls[e]) : 0.f;
+        s[r] = pr;
+        dp[r] = pr * (dp[r] - de[e]);
+      }
     }
     // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
 #pragma unroll
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
   constexpr int PER = T::PER;
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kRows * T::RS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[kRows * T::RS];
-  __shared__ int kps[kRows];
+  __shared__ __attribute__((aligned(16))) int kps[kRows];
   __shared__ int qmax_red[kBwdWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
@@ -444,10 +453,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Vs, lane, st), gf[st], dp, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool vis = kps[out_row(r, lane)] <= qp;
-      const float pr = vis ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2) : 0.f;
-      dp[r] = pr * (dp[r] - del);
+    for (int i = 0; i < 4; ++i) {
+      const i32x4 kk = *(const i32x4*)(kps + 8 * i + 4 * h);  // keys of registers 4i .. 4i+3
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * i + e;
+        const float pr = (kk[e] <= qp) ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2) : 0.f;
+        dp[r] = pr * (dp[r] - del);
+      }
     }
     // dQ^T += K^T dS^T (scale applied at the end)
 #pragma unroll
