@@ -187,8 +187,12 @@ __device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 
 // ---------------------------------------------------------------------------
 // dK and dV of 128 keys per workgroup.
 
+// Two workgroups per CU where the registers allow (head_dim <= 64): the waves of
+// one then hide the barrier and LDS latency of the other.
+constexpr int dkdv_resident(int dp) { return dp <= 64 ? 2 : 1; }
+
 template <int DP>
-__global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(BwdParams p) {
   using T = Tile<DP>;
   constexpr int NS = DP / 16;  // k-steps over head_dim
   constexpr int NB = DP / 32;  // 32-row blocks of head_dim
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void dkdv_kernel(BwdParams p) {
 // dQ of 128 query rows per workgroup.
 
 template <int DP>
-__global__ __launch_bounds__(kBwdThreads, 1) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   using T = Tile<DP>;
   constexpr int NS = DP / 16;
   constexpr int NB = DP / 32;
