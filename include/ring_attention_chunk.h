@@ -150,9 +150,11 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
 
 /* Device workspace, in bytes, that ra_ring_attention_backward needs: the
  * chunk table, the query and key positions (4 bytes per query row and per
- * key), per-32-row position bounds, and delta (fp32 per (batch, head, query)
- * row). A multiple of 256. */
-size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int64_t q_len, int64_t total_keys, int n_chunks);
+ * key), per-32-row position bounds, delta (fp32 per (batch, head, query)
+ * row) and, when the query rows alone cannot fill the GPU, fp32 partial dq of
+ * up to 8 key ranges. A multiple of 256. */
+size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys,
+                                        int n_chunks);
 
 /* Gradients of ring_attention for this device's share.
  * "Ring Attention: Distributed Reads with Online Softmax", section "Backward

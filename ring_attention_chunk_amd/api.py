@@ -81,7 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_ring_attention.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                       ctypes.POINTER(KVChunk), i32, i32, f32, vp, sz, vp, vp, vp]
     lib.ra_ring_attention.restype = i32
-    lib.ra_ring_backward_workspace_bytes.argtypes = [i32, i32, i64, i64, i32]
+    lib.ra_ring_backward_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32]
     lib.ra_ring_backward_workspace_bytes.restype = sz
     lib.ra_ring_attention_backward.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                                ctypes.POINTER(KVChunk), i32, i32, f32, vp, vp, vp, vp, sz, vp, vp,
@@ -236,8 +236,9 @@ def workspace_bytes(query_shape, key_lengths, n_q_segments: int = 1) -> int:
 
 def backward_workspace_bytes(query_shape, key_lengths) -> int:
     """Bytes of device workspace ``ring_attention_backward`` needs for this shape."""
-    B, Hq, Lq, _ = query_shape
-    return int(load_library().ra_ring_backward_workspace_bytes(B, Hq, Lq, int(sum(key_lengths)), len(key_lengths)))
+    B, Hq, Lq, d = query_shape
+    return int(load_library().ra_ring_backward_workspace_bytes(B, Hq, d, Lq, int(sum(key_lengths)),
+                                                               len(key_lengths)))
 
 
 def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global_offset: QOffset = 0,
@@ -375,7 +376,7 @@ def ring_attention_backward(query, key_chunks: Sequence, value_chunks: Sequence,
         scale = 1.0 / math.sqrt(d)
     lens = [int(k.shape[2]) for k in key_chunks]
     total = sum(lens)
-    need = lib.ra_ring_backward_workspace_bytes(B, Hq, Lq, total, n)
+    need = lib.ra_ring_backward_workspace_bytes(B, Hq, d, Lq, total, n)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace.numel() < need or workspace.data_ptr() % 256 != 0:

@@ -89,6 +89,8 @@ struct BwdParams {
   int causal;
   float scale;
   float c2;  // scale * log2(e)
+  int dq_split;    // key-tile ranges of the dQ kernel (1: dQ written directly)
+  float* dq_part;  // [dq_split][B * Hq * Lq][d] unscaled partial dQ when dq_split > 1 (workspace)
 };
 
 // Row address of key j (chunk `c` holds it); the cursor only moves forward.
@@ -373,7 +375,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int n_qt = (int)((p.Lq + kGroupRows - 1) / kGroupRows);
   const int qt = blockIdx.x % n_qt;
-  const int bh = blockIdx.x / n_qt;
+  const int rest = blockIdx.x / n_qt;
+  const int bh = rest % (p.B * p.Hq), split = rest / (p.B * p.Hq);
   const int hq = bh % p.Hq, b = bh / p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);
 
@@ -408,8 +411,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NB; ++db) dqT[db] = f32x16{};
 
-  // key tiles of 32 in list order, skipping tiles after every query of the workgroup
-  const int n_kt = (int)((p.Lk + kRows - 1) / kRows);
+  // key tiles of 32 in list order (this workgroup's range of them when the key range is split),
+  // skipping tiles after every query of the workgroup
+  const int n_kt_all = (int)((p.Lk + kRows - 1) / kRows);
+  const int per_split = (n_kt_all + p.dq_split - 1) / p.dq_split;
+  const int t_beg = split * per_split;
+  const int n_kt = min(n_kt_all, t_beg + per_split);
   auto advance = [&](int& t) {
     while (++t < n_kt)
       if (!p.causal || p.ktile_min[t] <= qmax) return true;
@@ -437,7 +444,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
     if (tid < kRows) pkp = (j0 + tid < p.Lk) ? p.kpos[j0 + tid] : kPosMax;
   };
 
-  int t = -1;
+  int t = t_beg - 1;
   bool have = advance(t);
   if (have) fetch(t);
   while (have) {
@@ -477,19 +484,33 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   }
 
   if (qvalid) {
-    float* dqr = p.dq + row * p.d;
+    // one range: dQ itself; several: this range's unscaled partial, summed by dq_reduce_kernel
+    const bool direct = p.dq_split == 1;
+    const float sc = direct ? p.scale : 1.f;
+    float* dqr = direct ? p.dq + row * p.d
+                        : p.dq_part + ((int64_t)split * p.B * p.Hq * p.Lq + row) * p.d;
 #pragma unroll
     for (int db = 0; db < NB; ++db)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int col = db * 32 + 8 * k + 4 * h;
         if (col < p.d) {
-          const f32x4 v = {dqT[db][4 * k] * p.scale, dqT[db][4 * k + 1] * p.scale, dqT[db][4 * k + 2] * p.scale,
-                           dqT[db][4 * k + 3] * p.scale};
+          const f32x4 v = {dqT[db][4 * k] * sc, dqT[db][4 * k + 1] * sc, dqT[db][4 * k + 2] * sc,
+                           dqT[db][4 * k + 3] * sc};
           *(f32x4*)(dqr + col) = v;
         }
       }
   }
+}
+
+// dQ = scale * (sum of the key-range partials, in range order); 16 bytes per thread.
+__global__ __launch_bounds__(256) void dq_reduce_kernel(int64_t n4, int ns, const f32x4* __restrict__ part,
+                                                        f32x4* __restrict__ dq, float scale) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n4) return;
+  f32x4 acc = part[e];
+  for (int s = 1; s < ns; ++s) acc += part[(int64_t)s * n4 + e];
+  dq[e] = acc * scale;
 }
 
 // ---------------------------------------------------------------------------
@@ -500,10 +521,21 @@ using namespace ra_host;
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t chunks, qpos, kpos, qblk, ktile, table_end, delta, total;
+  size_t chunks, qpos, kpos, qblk, ktile, table_end, delta, part, total;
+  int dq_split;
 };
 
-BwdLayout bwd_layout(int batch, int q_heads, int64_t q_len, int64_t total_keys, int n_chunks) {
+// Key-range split of the dQ kernel: enough workgroups for two per CU, each range
+// at least 16 key tiles of 32, at most 8 ranges.
+int choose_dq_split(int batch, int q_heads, int64_t q_len, int64_t total_keys) {
+  const int64_t base = ((q_len + kGroupRows - 1) / kGroupRows) * (int64_t)batch * q_heads;
+  const int64_t tiles = (total_keys + kRows - 1) / kRows;
+  int ns = 1;
+  while (base > 0 && base * ns < 2 * 256 && ns < 8 && tiles / (2 * ns) >= 16) ns *= 2;
+  return ns;
+}
+
+BwdLayout bwd_layout(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys, int n_chunks) {
   BwdLayout L;
   const int64_t nqb = (q_len + kRows - 1) / kRows, nkt = (total_keys + kRows - 1) / kRows;
   L.chunks = 0;
@@ -513,8 +545,13 @@ BwdLayout bwd_layout(int batch, int q_heads, int64_t q_len, int64_t total_keys, 
   L.ktile = L.qblk + al256(sizeof(int) * (size_t)(nqb > 0 ? nqb : 1));
   L.table_end = L.ktile + al256(sizeof(int) * (size_t)(nkt > 0 ? nkt : 1));
   L.delta = L.table_end;
-  L.total = L.delta + al256(sizeof(float) * (size_t)(batch > 0 ? batch : 0) * (size_t)(q_heads > 0 ? q_heads : 0) *
-                            (size_t)(q_len > 0 ? q_len : 0));
+  const size_t rows = (size_t)(batch > 0 ? batch : 0) * (size_t)(q_heads > 0 ? q_heads : 0) *
+                      (size_t)(q_len > 0 ? q_len : 0);
+  L.part = L.delta + al256(sizeof(float) * rows);
+  L.dq_split = (batch > 0 && q_heads > 0 && q_len > 0) ? choose_dq_split(batch, q_heads, q_len, total_keys) : 1;
+  L.total = L.part + (L.dq_split > 1 ? al256(sizeof(float) * (size_t)L.dq_split * rows *
+                                             (size_t)(head_dim > 0 ? head_dim : 0))
+                                     : 0);
   return L;
 }
 
@@ -529,8 +566,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timer_begin(s);
-  hipLaunchKernelGGL((dq_kernel<DP>), dim3((unsigned)(n_qt * p.B * p.Hq)), dim3(kBwdThreads), 0, s, p);
+  hipLaunchKernelGGL((dq_kernel<DP>), dim3((unsigned)(n_qt * p.B * p.Hq * p.dq_split)), dim3(kBwdThreads), 0, s,
+                     p);
   timer_end(s);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.dq_split == 1) return e;
+  const int64_t n4 = (int64_t)p.B * p.Hq * p.Lq * p.d / 4;
+  hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, n4, p.dq_split,
+                     (const f32x4*)p.dq_part, (f32x4*)p.dq, p.scale);
   return hipGetLastError();
 }
 
@@ -538,11 +581,12 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
 
 extern "C" {
 
-size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int64_t q_len, int64_t total_keys, int n_chunks) {
+size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys,
+                                        int n_chunks) {
   if (n_chunks < 0) n_chunks = 0;
   if (q_len < 0) q_len = 0;
   if (total_keys < 0) total_keys = 0;
-  return bwd_layout(batch, q_heads, q_len, total_keys, n_chunks).total;
+  return bwd_layout(batch, q_heads, head_dim, q_len, total_keys, n_chunks).total;
 }
 
 int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
@@ -585,7 +629,7 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
   const int64_t blocks_q = ((lq + kGroupRows - 1) / kGroupRows) * batch * q_heads;
   const int64_t blocks_k = ((lk + kGroupRows - 1) / kGroupRows) * batch * kv_heads;
   if (blocks_q > 0x7fffffffLL || blocks_k > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
-  const BwdLayout L = bwd_layout(batch, q_heads, lq, lk, n_chunks);
+  const BwdLayout L = bwd_layout(batch, q_heads, head_dim, lq, lk, n_chunks);
   if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0)
     return fail(RA_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);
@@ -663,6 +707,8 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.c2 = scale * kLog2e;
+  p.dq_split = L.dq_split;
+  p.dq_part = L.dq_split > 1 ? (float*)(ws + L.part) : nullptr;
 
   const int64_t rows = (int64_t)batch * q_heads * lq;
   int lpr = 1, sh = 0;

@@ -158,5 +158,10 @@ def test_backward_validation_codes(lib):
     assert bwd(dq=None) == 1
     assert bwd() == 6  # no workspace
     assert b"workspace" in lib.ra_last_error()
-    need = lib.ra_ring_backward_workspace_bytes(1, 2, 4, 8, 1)
+    need = lib.ra_ring_backward_workspace_bytes(1, 2, 64, 4, 8, 1)
     assert need % 256 == 0 and need >= 4 * (4 + 8) + 4 * 2 * 4
+    # a short share with many keys gets room for partial dq of several key ranges
+    small = lib.ra_ring_backward_workspace_bytes(1, 8, 64, 4096, 32768, 8)
+    assert small >= 2 * 8 * 4096 * 64 * 4
+    big = lib.ra_ring_backward_workspace_bytes(1, 32, 128, 8192, 65536, 8)
+    assert big < 32 * 8192 * 128 * 4  # enough query rows: no partials
