@@ -8,9 +8,13 @@ section "Backward must aggregate shared dependencies": check the distributed
 operation against a single-device reference, gradients included).
 """
 
+import importlib.util
+import inspect
+
 import numpy as np
 import pytest
 
+import oracle.backward as ob
 from oracle import attention, attention_backward
 
 
@@ -133,3 +137,67 @@ def test_closed_forms():
     # shifting every key by the same vector c adds scale*<q, c> to a row's scores: softmax and dq do
     # not change, and sum_j dk_j = scale * sum_i (sum_j ds_ij) q_i = 0 since each row of ds sums to 0
     assert np.max(np.abs(g["dk"].sum(axis=2))) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each plausible slip in the gradient oracle's source must break the finite-difference
+# pin (GQA with two query heads on one key/value head, causal, chunks out of position order)
+
+MUTANTS = [
+    ("no softmax-Jacobian correction", "(dp - (p * dp).sum(axis=1, keepdims=True))", "dp"),
+    ("dq without the scale", "dq[b, h, r0:r1] = scale * (ds @ k[b, hk])", "dq[b, h, r0:r1] = ds @ k[b, hk]"),
+    ("dk from p instead of ds", "scale * (ds.T @ q[b, h, r0:r1])", "scale * (p.T @ q[b, h, r0:r1])"),
+    ("dv from q instead of dout", "dv[b, hk] += p.T @ g", "dv[b, hk] += p.T @ q[b, h, r0:r1]"),
+    ("strict causal boundary", "kpos[None, :] <= qpos[r0:r1, None]", "kpos[None, :] < qpos[r0:r1, None]"),
+    ("GQA group overwrites dk", "dk[b, hk] += scale", "dk[b, hk] = scale"),
+    ("dp against k instead of v", "dp = g @ v[b, hk].T", "dp = g @ k[b, hk].T"),
+]
+
+
+def _fd_error(fn):
+    B, Hq, Hkv, Lq, d = 1, 2, 1, 4, 3
+    lens, offs = [3, 2], [2, 0]
+    q = _rand((B, Hq, Lq, d), 1)
+    k = _rand((B, Hkv, sum(lens), d), 2, 1.5)
+    v = _rand((B, Hkv, sum(lens), d), 3)
+    do = _rand((B, Hq, Lq, d), 4)
+    qpos = np.array([0, 1, 3, 4])
+    cut = lens[0]
+
+    def chunks(kk, vv):
+        return [kk[:, :, :cut], kk[:, :, cut:]], [vv[:, :, :cut], vv[:, :, cut:]]
+
+    kc, vc = chunks(k, v)
+    g = fn(q, kc, vc, do, qpos, offs, causal=True, scale=0.7)
+    worst, eps = 0.0, 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        for idx in np.ndindex(x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            ap, am = dict(args), dict(args)
+            ap[name[1]], am[name[1]] = xp, xm
+            lp = _loss(ap["q"], *chunks(ap["k"], ap["v"]), do, qpos, offs, True, 0.7)
+            lm = _loss(am["q"], *chunks(am["k"], am["v"]), do, qpos, offs, True, 0.7)
+            worst = max(worst, abs((lp - lm) / (2 * eps) - g[name][idx]))
+    return worst
+
+
+def _mutated(old, new):
+    src = inspect.getsource(ob)
+    assert src.count(old) == 1, old
+    spec = importlib.util.spec_from_loader("oracle._backward_mutant", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), "oracle_backward_mutant", "exec"), mod.__dict__)
+    return mod.attention_backward
+
+
+def test_finite_difference_pin_accepts_the_oracle():
+    assert _fd_error(ob.attention_backward) <= 1e-7
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_finite_difference_pin_catches_planted_mistake(name, old, new):
+    assert _fd_error(_mutated(old, new)) > 1e-4, name
