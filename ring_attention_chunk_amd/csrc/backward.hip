@@ -77,8 +77,8 @@ struct BwdParams {
   float* delta;        // [B, Hq, Lq] (workspace)
   const int* qpos;     // [Lq] query positions (kPosAllQ when not causal)
   const int* kpos;     // [Lk] key positions in list order
-  const int* qblk_max; // [ceil(Lq / 32)] largest query position of each 32-row block
-  const int* ktile_min;// [ceil(Lk / 32)] smallest key position of each 32-key tile
+  const int* qblk;     // [ceil(Lq / 32)][2] smallest and largest query position of each 32-row block
+  const int* ktile;    // [ceil(Lk / 32)][2] smallest and largest key position of each 32-key tile
   const BwdChunk* chunks;
   float* dq;           // [B, Hq, Lq, d]
   float* dk;           // [B, Hkv, Lk, d]
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
   __shared__ __attribute__((aligned(16))) float lse2s[kRows];
   __shared__ __attribute__((aligned(16))) float dels[kRows];
   __shared__ __attribute__((aligned(16))) int qps[kRows];
-  __shared__ int kmin_red[kBwdWaves];
+  __shared__ int kmin_red[2 * kBwdWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int n_kt = (int)((p.Lk + kGroupRows - 1) / kGroupRows);
@@ -236,13 +236,23 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
     }
     if (kvalid) kp = p.kpos[j];
   }
-  // smallest key position of the workgroup: query blocks entirely before it see nothing here
-  int wk = kp;
-  for (int o = 32; o > 0; o >>= 1) wk = min(wk, __shfl_xor(wk, o));
-  if (lane == 0) kmin_red[wave] = wk;
+  // smallest and largest key position of the workgroup: query blocks entirely before the smallest
+  // see nothing here, and blocks entirely at or after the largest see everything (no mask)
+  int wk = kp, wx = kvalid ? kp : kPosMinQ;
+  for (int o = 32; o > 0; o >>= 1) {
+    wk = min(wk, __shfl_xor(wk, o));
+    wx = max(wx, __shfl_xor(wx, o));
+  }
+  if (lane == 0) {
+    kmin_red[wave] = wk;
+    kmin_red[kBwdWaves + wave] = wx;
+  }
   __syncthreads();
-  int kmin = kmin_red[0];
-  for (int w = 1; w < kBwdWaves; ++w) kmin = min(kmin, kmin_red[w]);
+  int kmin = kmin_red[0], kmax = kmin_red[kBwdWaves];
+  for (int w = 1; w < kBwdWaves; ++w) {
+    kmin = min(kmin, kmin_red[w]);
+    kmax = max(kmax, kmin_red[kBwdWaves + w]);
+  }
 
   f32x16 dkT[NB], dvT[NB];
 #pragma unroll
@@ -259,7 +269,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
         qb = 0;
         if (++g >= group) return false;
       }
-      if (!p.causal || p.qblk_max[qb] >= kmin) return true;
+      if (!p.causal || p.qblk[2 * qb + 1] >= kmin) return true;
     }
   };
   u32x4 pq[PER], pg[PER];
@@ -300,6 +310,9 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
       qps[tid] = pp;
     }
     __syncthreads();
+    // every query of this block sees every key of the workgroup: no mask (rows past the last
+    // query are zero in LDS, with lse and delta 0, and contribute nothing either way)
+    const bool full = !p.causal || p.qblk[2 * cqb] >= kmax;
     have = advance(cg, cqb);
     if (have) fetch(cg, cqb);  // in flight during the matrix work below
 
@@ -311,18 +324,34 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Gs, lane, st), vf[st], dp, 0, 0, 0);
     }
     // registers 4i .. 4i+3 hold queries 8i + 4h .. +3: one 16-byte LDS read per table and group
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q0 = 8 * i + 4 * h;
-      const f32x4 ls = *(const f32x4*)(lse2s + q0);
-      const f32x4 de = *(const f32x4*)(dels + q0);
-      const i32x4 qq = *(const i32x4*)(qps + q0);
+      for (int i = 0; i < 4; ++i) {
+        const int q0 = 8 * i + 4 * h;
+        const f32x4 ls = *(const f32x4*)(lse2s + q0);
+        const f32x4 de = *(const f32x4*)(dels + q0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * i + e;
-        const float pr = (kp <= qq[e]) ? __builtin_amdgcn_exp2f(s[r] * p.c2 - ls[e]) : 0.f;
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - de[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * i + e;
+          const float pr = __builtin_amdgcn_exp2f(s[r] * p.c2 - ls[e]);
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - de[e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q0 = 8 * i + 4 * h;
+        const f32x4 ls = *(const f32x4*)(lse2s + q0);
+        const f32x4 de = *(const f32x4*)(dels + q0);
+        const i32x4 qq = *(const i32x4*)(qps + q0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * i + e;
+          const float pr = (kp <= qq[e]) ? __builtin_amdgcn_exp2f(s[r] * p.c2 - ls[e]) : 0.f;
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - de[e]);
+        }
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
@@ -370,7 +399,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 Ks[kRows * T::RS];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[kRows * T::RS];
   __shared__ __attribute__((aligned(16))) int kps[kRows];
-  __shared__ int qmax_red[kBwdWaves];
+  __shared__ int qmax_red[2 * kBwdWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int n_qt = (int)((p.Lq + kGroupRows - 1) / kGroupRows);
@@ -400,12 +429,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   const float lse2 = (lsev == -INFINITY) ? 0.f : lsev * kLog2e;
   const float del = qvalid ? p.delta[row] : 0.f;
   const int qp = qvalid ? p.qpos[i] : kPosMinQ;
-  int wq = qp;
-  for (int o = 32; o > 0; o >>= 1) wq = max(wq, __shfl_xor(wq, o));
-  if (lane == 0) qmax_red[wave] = wq;
+  int wq = qp, wn = qvalid ? qp : kPosMax;
+  for (int o = 32; o > 0; o >>= 1) {
+    wq = max(wq, __shfl_xor(wq, o));
+    wn = min(wn, __shfl_xor(wn, o));
+  }
+  if (lane == 0) {
+    qmax_red[wave] = wq;
+    qmax_red[kBwdWaves + wave] = wn;
+  }
   __syncthreads();
-  int qmax = qmax_red[0];
-  for (int w = 1; w < kBwdWaves; ++w) qmax = max(qmax, qmax_red[w]);
+  int qmax = qmax_red[0], qmin = qmax_red[kBwdWaves];
+  for (int w = 1; w < kBwdWaves; ++w) {
+    qmax = max(qmax, qmax_red[w]);
+    qmin = min(qmin, qmax_red[kBwdWaves + w]);
+  }
 
   f32x16 dqT[NB];
 #pragma unroll
@@ -419,7 +457,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   const int n_kt = min(n_kt_all, t_beg + per_split);
   auto advance = [&](int& t) {
     while (++t < n_kt)
-      if (!p.causal || p.ktile_min[t] <= qmax) return true;
+      if (!p.causal || p.ktile[2 * t] <= qmax) return true;
     return false;
   };
   // staging cursors: each thread's pieces keep their row slot from tile to tile
@@ -453,6 +491,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
     T::put(Vs, tid, pv);
     if (tid < kRows) kps[tid] = pkp;
     __syncthreads();
+    // every key of this (complete) tile is seen by every query of the workgroup: no mask. The
+    // last tile keeps it: its missing keys have zero rows, but exp(-lse) of such a key could
+    // overflow and turn 0 * inf into NaN
+    const bool full = (int64_t)(t + 1) * kRows <= p.Lk && (!p.causal || p.ktile[2 * t + 1] <= qmin);
     have = advance(t);
     if (have) fetch(t);  // in flight during the matrix work below
 
@@ -463,14 +505,19 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Ks, lane, st), qf[st], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Vs, lane, st), gf[st], dp, 0, 0, 0);
     }
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i32x4 kk = *(const i32x4*)(kps + 8 * i + 4 * h);  // keys of registers 4i .. 4i+3
+      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2) * (dp[r] - del);
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * i + e;
-        const float pr = (kk[e] <= qp) ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2) : 0.f;
-        dp[r] = pr * (dp[r] - del);
+      for (int i = 0; i < 4; ++i) {
+        const i32x4 kk = *(const i32x4*)(kps + 8 * i + 4 * h);  // keys of registers 4i .. 4i+3
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * i + e;
+          const float pr = (kk[e] <= qp) ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2) : 0.f;
+          dp[r] = pr * (dp[r] - del);
+        }
       }
     }
     // dQ^T += K^T dS^T (scale applied at the end)
@@ -542,8 +589,8 @@ BwdLayout bwd_layout(int batch, int q_heads, int head_dim, int64_t q_len, int64_
   L.qpos = L.chunks + al256(sizeof(BwdChunk) * (size_t)(n_chunks > 0 ? n_chunks : 1));
   L.kpos = L.qpos + al256(sizeof(int) * (size_t)(q_len > 0 ? q_len : 1));
   L.qblk = L.kpos + al256(sizeof(int) * (size_t)(total_keys > 0 ? total_keys : 1));
-  L.ktile = L.qblk + al256(sizeof(int) * (size_t)(nqb > 0 ? nqb : 1));
-  L.table_end = L.ktile + al256(sizeof(int) * (size_t)(nkt > 0 ? nkt : 1));
+  L.ktile = L.qblk + al256(2 * sizeof(int) * (size_t)(nqb > 0 ? nqb : 1));
+  L.table_end = L.ktile + al256(2 * sizeof(int) * (size_t)(nkt > 0 ? nkt : 1));
   L.delta = L.table_end;
   const size_t rows = (size_t)(batch > 0 ? batch : 0) * (size_t)(q_heads > 0 ? q_heads : 0) *
                       (size_t)(q_len > 0 ? q_len : 0);
@@ -670,12 +717,18 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
   for (int64_t qb = 0; qb * kRows < lq; ++qb) {
     int mx = kPosMinQ;
     for (int64_t i = qb * kRows; i < lq && i < (qb + 1) * kRows; ++i) mx = hqp[i] > mx ? hqp[i] : mx;
-    hqb[qb] = mx;
+    int mn = kPosMax;
+    for (int64_t i = qb * kRows; i < lq && i < (qb + 1) * kRows; ++i) mn = hqp[i] < mn ? hqp[i] : mn;
+    hqb[2 * qb] = mn;
+    hqb[2 * qb + 1] = mx;
   }
   for (int64_t t = 0; t * kRows < lk; ++t) {
     int mn = kPosMax;
     for (int64_t j = t * kRows; j < lk && j < (t + 1) * kRows; ++j) mn = hkp[j] < mn ? hkp[j] : mn;
-    hkt[t] = mn;
+    int mx = kPosMinQ;
+    for (int64_t j = t * kRows; j < lk && j < (t + 1) * kRows; ++j) mx = hkp[j] > mx ? hkp[j] : mx;
+    hkt[2 * t] = mn;
+    hkt[2 * t + 1] = mx;
   }
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(workspace, host, L.table_end, hipMemcpyHostToDevice, hs);
@@ -691,8 +744,8 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
   p.delta = (float*)(ws + L.delta);
   p.qpos = (const int*)(ws + L.qpos);
   p.kpos = (const int*)(ws + L.kpos);
-  p.qblk_max = (const int*)(ws + L.qblk);
-  p.ktile_min = (const int*)(ws + L.ktile);
+  p.qblk = (const int*)(ws + L.qblk);
+  p.ktile = (const int*)(ws + L.ktile);
   p.chunks = (const BwdChunk*)(ws + L.chunks);
   p.dq = dq;
   p.dk = dk;
