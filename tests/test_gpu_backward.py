@@ -156,19 +156,23 @@ def test_backward_full_size(i):
 
 
 def test_backward_very_negative_scores_with_ragged_last_tile():
-    """Scores near -130 make exp(-lse) overflow fp32. The last key tile (100 keys: 4 of 32 missing)
-    must still be masked so that its missing keys give 0, not 0 * inf = NaN, in dq."""
+    """Every score near -160 (lse near -110) makes exp(-lse) overflow fp32. The last key tile (100
+    keys: 28 of 128 missing in the last workgroup, 4 of 32 in the last tile) must still be masked so
+    that its missing keys give 0, not 0 * inf = NaN, in dq. The scores are made negative by a large
+    query against keys whose mean is -1 and whose spread is 1, so that the common part of the keys
+    (which the exact dq cancels) is no larger than the rest."""
     _say("backward very negative scores")
     g = torch.Generator().manual_seed(12)
     d, Lq, Lk = 64, 64, 100
-    q = (4.0 * torch.ones(1, 2, Lq, d) + 0.1 * torch.randn(1, 2, Lq, d, generator=g)).to(torch.bfloat16)
-    k = (-4.0 * torch.ones(1, 2, Lk, d) + 0.5 * torch.randn(1, 2, Lk, d, generator=g)).to(torch.bfloat16)
+    q = (20.0 * torch.ones(1, 2, Lq, d) + 0.5 * torch.randn(1, 2, Lq, d, generator=g)).to(torch.bfloat16)
+    k = (-1.0 + torch.randn(1, 2, Lk, d, generator=g)).to(torch.bfloat16)
     v = torch.randn(1, 2, Lk, d, generator=g).to(torch.bfloat16)
     dout = torch.randn(1, 2, Lq, d, generator=g).to(torch.bfloat16)
     qd, kd, vd, dd = (t.to(DEV) for t in (q, k, v, dout))
     out, lse = ra.ring_attention(qd, [kd], [vd], return_lse=True)
     dq, dks, dvs = ra.ring_attention_backward(qd, [kd], [vd], out, lse, dd)
     torch.cuda.synchronize()
+    print(f"  lse max {lse.max().item():.1f}", flush=True)
     assert lse.max().item() < -88.0  # exp(-lse) is beyond fp32
     ref = oracle.attention_backward(q, [k], [v], dout)
     _compare("dq", _np(dq), ref["dq"])
