@@ -258,50 +258,21 @@ def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global
     """
     torch = _torch()
     lib = load_library()
-    if len(key_chunks) != len(value_chunks):
-        raise RingAttentionError("key_chunks and value_chunks differ in length")
-    _require_gpu(query, *key_chunks, *value_chunks)
-    if query.dim() != 4:
-        raise RingAttentionError("query must be [batch, q_heads, q_len, head_dim]")
+    Hkv, descs, n, segs, nseg = _marshal(query, key_chunks, value_chunks, q_global_offset, kv_global_offsets,
+                                         kv_position_strides)
     q = query.contiguous()
     B, Hq, Lq, d = q.shape
-    for t in list(key_chunks) + list(value_chunks):
-        if t.dtype != q.dtype:
-            raise RingAttentionError("query, keys and values must share a dtype")
-    if kv_global_offsets is None:
-        kv_global_offsets, acc = [], 0
-        for k in key_chunks:
-            kv_global_offsets.append(acc)
-            acc += int(k.shape[2])
-    if len(kv_global_offsets) != len(key_chunks):
-        raise RingAttentionError("one global offset per chunk is required")
-    if kv_position_strides is None:
-        kv_position_strides = [1] * len(key_chunks)
-    if len(kv_position_strides) != len(key_chunks):
-        raise RingAttentionError("one position stride per chunk is required")
-    Hkv = int(key_chunks[0].shape[1]) if key_chunks else Hq
-    n = len(key_chunks)
-    descs = (KVChunk * max(n, 1))()
-    for i, (k, v, off, ps) in enumerate(zip(key_chunks, value_chunks, kv_global_offsets, kv_position_strides)):
-        descs[i] = _chunk_desc(k, v, off, B, Hkv, d, ps)
-    if isinstance(q_global_offset, int):
-        segs_py = [(int(q_global_offset), Lq, 1)]
-    else:
-        segs_py = [(int(g[0]), int(g[1]), int(g[2]) if len(g) > 2 else 1) for g in q_global_offset]
-    if sum(g[1] for g in segs_py) != Lq:
-        raise RingAttentionError(f"query segments cover {sum(g[1] for g in segs_py)} rows, query has {Lq}")
-    segs = (QSegment * len(segs_py))(*[QSegment(n_, o, ps) for o, n_, ps in segs_py])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     total_keys = sum(int(k.shape[2]) for k in key_chunks)
-    need = lib.ra_ring_workspace_bytes(B, Hq, d, Lq, total_keys, n, len(segs_py))
+    need = lib.ra_ring_workspace_bytes(B, Hq, d, Lq, total_keys, n, nseg)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace.numel() < need or workspace.data_ptr() % 256 != 0:
         raise RingAttentionError(f"workspace must hold {need} bytes at a 256-byte aligned address")
     out = torch.empty((B, Hq, Lq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
-    st = lib.ra_ring_attention(_dtype_code(q), B, Hq, Hkv, d, q.data_ptr(), segs, len(segs_py), descs, n,
+    st = lib.ra_ring_attention(_dtype_code(q), B, Hq, Hkv, d, q.data_ptr(), segs, nseg, descs, n,
                                int(bool(causal)), float(scale), workspace.data_ptr(), workspace.numel(),
                                out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q))
     _check(lib, st, "ring_attention")
