@@ -453,7 +453,7 @@ def main():
             "shape": f"{rows} rows x d={d}, fp32, 4 rotating buffer sets",
         }
         del sets, src, dst, srcs
-        if w.dtype == "bf16" and w.head_dim in (32, 64, 128):
+        if w.dtype == "bf16" and w.head_dim % 8 == 0:
             legs["ring_attention_backward"] = backward_leg(w, q, kc, vc, offs, args, torch, ra)
         result["legs"] = legs
 

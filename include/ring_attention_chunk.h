@@ -169,7 +169,8 @@ size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int head_dim, in
  *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
  * where the sums over i run over every query head sharing k_j's head (GQA).
  *  dtype       RA_BF16 only (bf16 matrix cores, fp32 accumulation); other
- *              types return RA_ERR_UNSUPPORTED. head_dim is 32, 64 or 128.
+ *              types return RA_ERR_UNSUPPORTED. head_dim is a multiple of 8
+ *              (8 .. 128).
  *  q, dout     [B,Hq,q_len,d] bf16; out [B,Hq,q_len,d] fp32 and lse
  *              [B,Hq,q_len] fp32 as ra_ring_attention returned them for the
  *              same inputs (lse must not be NULL there).

@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
       int r, c8;
       pq[k] = u32x4{0u, 0u, 0u, 0u};
       pg[k] = u32x4{0u, 0u, 0u, 0u};
-      if (T::piece(tid, k, r, c8) && r < nrows) {
+      if (T::piece(tid, k, r, c8) && r < nrows && c8 * 8 < p.d) {
         pq[k] = *(const u32x4*)(p.q + (rowbase + r0 + r) * p.d + c8 * 8);
         pg[k] = *(const u32x4*)(p.dout + (rowbase + r0 + r) * p.d + c8 * 8);
       }
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
       int r, c8;
       pk[k] = u32x4{0u, 0u, 0u, 0u};
       pv[k] = u32x4{0u, 0u, 0u, 0u};
-      if (T::piece(tid, k, r, c8) && j0 + r < p.Lk) {
+      if (T::piece(tid, k, r, c8) && j0 + r < p.Lk && c8 * 8 < p.d) {
         const int64_t off = key_offset(p, j0 + r, b, hk, cur[k]);
         pk[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].k + off + c8 * 8);
         pv[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].v + off + c8 * 8);
@@ -645,8 +645,8 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
   int st = check_dims(dtype, batch, q_heads, kv_heads, head_dim);
   if (st) return st;
   if (dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs");
-  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
-    return fail(RA_ERR_UNSUPPORTED, "the backward pass takes head_dim 32, 64 or 128 (got %d)", head_dim);
+  if (head_dim % 8 != 0)
+    return fail(RA_ERR_UNSUPPORTED, "the backward pass takes head_dim a multiple of 8 (got %d)", head_dim);
   if (n_q_segments < 1 || !q_segments) return fail(RA_ERR_NULL, "at least one query segment is required");
   if (n_chunks < 0 || (n_chunks > 0 && !chunks)) return fail(RA_ERR_NULL, "chunk array missing");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(RA_ERR_SHAPE, "scale must be finite and > 0");
@@ -773,9 +773,11 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
                      lpr, sh, (const __bf16*)dout, out, p.delta);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "ring_attention_backward delta launch");
-  if (head_dim == 32)
+  // tiles are DP = 32, 64 or 128 columns wide; columns past head_dim are zero in LDS and registers
+  // and are never written out
+  if (head_dim <= 32)
     e = launch_bwd<32>(p, hs);
-  else if (head_dim == 64)
+  else if (head_dim <= 64)
     e = launch_bwd<64>(p, hs);
   else
     e = launch_bwd<128>(p, hs);

@@ -153,7 +153,7 @@ def test_backward_validation_codes(lib):
                                               ws, wsb, dq, FAKE, FAKE, None)
 
     assert bwd(dtype=0) == 4  # fp32: not supported by the backward kernels
-    assert bwd(d=40) == 4
+    assert bwd(d=36) == 4  # not a multiple of 8
     assert bwd(Hq=3) == 2
     assert bwd(dq=None) == 1
     assert bwd() == 6  # no workspace

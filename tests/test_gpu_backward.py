@@ -47,6 +47,10 @@ CASES = [
     ("d64_striped", 1, 2, 2, 64, [(3, 150)], [(j, 150) for j in wl.ring_order(3, 4)], True, 4),
     ("d128_nc_one_chunk", 1, 2, 1, 128, [(0, 129)], [(0, 257)], False, 1),
     ("d64_causal_rows_before_keys", 1, 2, 2, 64, [(0, 96)], [(50, 100)], True, 1),
+    # head dims that are not a tile width: columns past head_dim are zero-padded in the kernels
+    ("d40_causal_gqa", 1, 4, 2, 40, [(100, 150)], [(0, 90), (90, 170)], True, 1),
+    ("d16_nc", 1, 2, 2, 16, [(0, 70)], [(0, 33), (33, 60)], False, 1),
+    ("d96_causal", 1, 2, 2, 96, [(64, 130)], [(0, 100), (100, 94)], True, 1),
 ]
 
 
@@ -116,10 +120,10 @@ def test_backward_is_bit_reproducible_and_split_invariant_in_dq():
 
 def test_backward_errors_raise():
     _say("backward errors")
-    q = torch.randn(1, 2, 8, 40, device=DEV).to(torch.bfloat16)
-    out = torch.zeros(1, 2, 8, 40, device=DEV)
+    q = torch.randn(1, 2, 8, 36, device=DEV).to(torch.bfloat16)
+    out = torch.zeros(1, 2, 8, 36, device=DEV)
     lse = torch.zeros(1, 2, 8, device=DEV)
-    with pytest.raises(ra.RingAttentionError):  # head_dim 40 is not supported by the backward kernels
+    with pytest.raises(ra.RingAttentionError):  # head_dim 36 is not a multiple of 8
         ra.ring_attention_backward(q, [q], [q], out, lse, q)
     qf = torch.randn(1, 2, 8, 64, device=DEV)
     with pytest.raises(ra.RingAttentionError):  # fp32 inputs
