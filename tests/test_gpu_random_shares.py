@@ -1,0 +1,109 @@
+"""Seeded random small shares against the fp64 oracles (needs an MI355X).
+
+Each case draws a shape (batch, heads, GQA group, head_dim), a layout of
+global positions (contiguous runs in a random ring order, paired early/late
+chunks, or striped with a random step), random cuts of the key list into
+chunks (empty chunks included), and causal or not. The forward pass is
+checked on every case, the backward pass on every bf16 case whose head_dim
+is a multiple of 8. Tolerances are those of the other parity tests.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_chunk_amd as ra
+from ring_attention_chunk_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+N_CASES = 200
+
+
+def _case(seed):
+    g = np.random.default_rng([seed, 5150])
+    dtype = "f32" if g.random() < 0.2 else "bf16"
+    d = int(g.choice([3, 5, 16, 100, 128])) if dtype == "f32" else int(g.choice([8, 16, 24, 40, 64, 72, 96, 128]))
+    B = int(g.integers(1, 3))
+    Hkv = int(g.integers(1, 3))
+    Hq = Hkv * int(g.choice([1, 2, 4]))
+    causal = bool(g.random() < 0.7)
+    layout = str(g.choice(["contiguous", "zigzag", "striped"]))
+    step = 1
+    if layout == "contiguous":
+        P = int(g.integers(1, 6))
+        L = int(g.integers(1, 160))
+        r = int(g.integers(0, P))
+        order = wl.ring_order(r, P)
+        runs = [(j * L, L) for j in order]
+        q0 = r * L + int(g.integers(0, L))
+        qseg = [(q0, int(g.integers(1, L + 1)))]
+    elif layout == "zigzag":
+        P = int(g.integers(1, 5))
+        C = int(g.integers(1, 100))
+        r = int(g.integers(0, P))
+        runs = []
+        for j in wl.ring_order(r, P):
+            runs += [(j * C, C), ((2 * P - 1 - j) * C, C)]
+        qseg = [(r * C, C), ((2 * P - 1 - r) * C, C)]
+    else:
+        P = int(g.integers(2, 6))
+        L = int(g.integers(1, 160))
+        r = int(g.integers(0, P))
+        step = P
+        runs = [(j, L) for j in wl.ring_order(r, P)]
+        qseg = [(r, L)]
+    # cut the runs at random places (empty chunks allowed)
+    chunks = []
+    for o, n in runs:
+        cuts = sorted(int(x) for x in g.integers(0, n + 1, size=int(g.integers(0, 3))))
+        edges = [0] + cuts + [n]
+        chunks += [(o + step * a, b - a) for a, b in zip(edges[:-1], edges[1:])]
+    name = f"rand{seed}_{dtype}_d{d}_{layout}_{'c' if causal else 'nc'}"
+    return wl.custom(name, dtype, B, Hq, Hkv, d, qseg, chunks, causal, seed=seed, pos_stride=step)
+
+
+def _check(got, ref, dtype):
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got))
+    if dtype == "f32":
+        assert err.max() <= 1e-5, err.max()
+    else:
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_share(seed):
+    w = _case(seed)
+    print(f"[case] {w.name} B={w.batch} Hq={w.q_heads} Hkv={w.kv_heads} q={w.q_segments} chunks={w.chunks}",
+          flush=True)
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    out, lse = ra.ring_attention(q, kc, vc, w.q_runs, w.kv_offsets, causal=w.causal, return_lse=True,
+                                 kv_position_strides=w.kv_strides)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q.cpu(), [c.cpu() for c in kc], [c.cpu() for c in vc], wl.q_positions(w),
+                           w.kv_offsets, causal=w.causal, kv_strides=w.kv_strides)
+    _check(out.cpu().double().numpy(), ref["out"], w.dtype)
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isfinite(lse.cpu().numpy()), fin)
+    tol = 1e-5 if w.dtype == "f32" else 1e-2
+    assert np.abs(lse.cpu().double().numpy()[fin] - ref["lse"][fin]).max(initial=0.0) <= tol
+    if w.dtype != "bf16" or w.head_dim % 8 != 0 or w.lk == 0:
+        return
+    g = torch.Generator().manual_seed(zlib.crc32(w.name.encode()))
+    dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    dq, dks, dvs = ra.ring_attention_backward(q, kc, vc, out, lse, dout, w.q_runs, w.kv_offsets, causal=w.causal,
+                                              kv_position_strides=w.kv_strides)
+    torch.cuda.synchronize()
+    gref = oracle.attention_backward(q.cpu(), [c.cpu() for c in kc], [c.cpu() for c in vc], dout.cpu(),
+                                     wl.q_positions(w), w.kv_offsets, causal=w.causal, kv_strides=w.kv_strides)
+    for name, got in (("dq", dq), ("dk", torch.cat(dks, 2)), ("dv", torch.cat(dvs, 2))):
+        got = got.cpu().double().numpy()
+        want = gref[name]
+        e = np.abs(got - want)
+        assert np.all(np.isfinite(got)), name
+        assert e.max() <= 1e-2 * max(np.abs(want).max(), 1e-6), (name, e.max(), np.abs(want).max())
+        assert e.mean() <= 5e-3 * max(np.abs(want).mean(), 1e-6), (name, e.mean(), np.abs(want).mean())
