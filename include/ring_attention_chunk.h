@@ -98,10 +98,24 @@ typedef struct ra_q_segment {
  * and the row-wise maximum score m over this one chunk, computed as if it were
  * the only chunk (no mask). u is relative to m: u = sum_j exp(s_j - m) v_j,
  * l = sum_j exp(s_j - m). A chunk of length 0 yields (0, 0, -inf).
- * Writes u [B,Hq,q_len,d], l and m [B,Hq,q_len]. */
+ * Writes u [B,Hq,q_len,d], l and m [B,Hq,q_len].
+ *  workspace   optional device buffer (NULL, or 256-byte aligned) of
+ *              workspace_bytes. With at least ra_chunk_stats_workspace_bytes(...)
+ *              bytes, a grid too small to fill the GPU is completed by cutting
+ *              the chunk's keys into ranges whose partial statistics are merged
+ *              afterwards on `stream`; with less (or NULL) the call runs
+ *              uncut. The results agree to rounding either way; for a given
+ *              shape and workspace they are bit-identical from run to run. */
 int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, int head_dim,
                              const void* q, int64_t q_len, const ra_kv_chunk* chunk,
-                             float scale, float* u, float* l, float* m, void* stream);
+                             float scale, float* u, float* l, float* m,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace, in bytes, with which ra_attention_chunk_stats cuts the
+ * keys into ranges for this shape: fp32 partial statistics, (head_dim + 2)
+ * values per row and range. 0 when the query rows fill the GPU on their own
+ * (a multiple of 256 otherwise). */
+size_t ra_chunk_stats_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t chunk_len);
 
 /* merge_chunk_stats(acc, chunk), in place on acc.
  * Exercise page, hint 2 ("rescale to the shared new max"): with

@@ -13,6 +13,7 @@ The three calls keep the names of the exercise page
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 from typing import List, Optional, Sequence, Tuple, Union
@@ -24,6 +25,7 @@ RA_F32, RA_BF16 = 0, 1
 # exported symbols, as declared in include/ring_attention_chunk.h
 EXPORTS = (
     "ra_attention_chunk_stats",
+    "ra_chunk_stats_workspace_bytes",
     "ra_merge_chunk_stats",
     "ra_ring_workspace_bytes",
     "ra_ring_attention",
@@ -72,8 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.ra_attention_chunk_stats.argtypes = [i32, i32, i32, i32, i32, vp, i64, ctypes.POINTER(KVChunk), f32,
-                                             vp, vp, vp, vp]
+                                             vp, vp, vp, vp, sz, vp]
     lib.ra_attention_chunk_stats.restype = i32
+    lib.ra_chunk_stats_workspace_bytes.argtypes = [i32, i32, i32, i64, i64]
+    lib.ra_chunk_stats_workspace_bytes.restype = sz
     lib.ra_merge_chunk_stats.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.ra_merge_chunk_stats.restype = i32
     lib.ra_ring_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32, i32]
@@ -151,11 +155,18 @@ def _chunk_desc(k, v, offset: int, batch: int, kv_heads: int, head_dim: int, pos
                    int(pos_stride))
 
 
-def attention_chunk_stats(query, key_chunk, value_chunk, scale: Optional[float] = None):
+@functools.lru_cache(maxsize=256)
+def _stats_workspace_bytes(B: int, Hq: int, d: int, Lq: int, Lc: int) -> int:
+    return int(load_library().ra_chunk_stats_workspace_bytes(B, Hq, d, Lq, Lc))
+
+
+def attention_chunk_stats(query, key_chunk, value_chunk, scale: Optional[float] = None, workspace=None):
     """Statistics of one chunk: ``(u, l, m)`` (un-normalised numerator, denominator, row max).
 
     query [B, Hq, Lq, d]; key_chunk, value_chunk [B, Hkv, Lc, d] (bf16 or fp32, on the GPU).
-    Returns fp32 tensors u [B, Hq, Lq, d], l and m [B, Hq, Lq].
+    Returns fp32 tensors u [B, Hq, Lq, d], l and m [B, Hq, Lq]. When the query rows alone cannot
+    fill the GPU, a device workspace for key-range partials is allocated (torch) unless one is
+    given.
     """
     torch = _torch()
     lib = load_library()
@@ -173,8 +184,14 @@ def attention_chunk_stats(query, key_chunk, value_chunk, scale: Optional[float] 
     u = torch.empty((B, Hq, Lq, d), dtype=torch.float32, device=q.device)
     l = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
     m = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    need = _stats_workspace_bytes(B, Hq, d, Lq, int(key_chunk.shape[2]))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() if workspace is not None else 0
     st = lib.ra_attention_chunk_stats(_dtype_code(q), B, Hq, Hkv, d, q.data_ptr(), Lq, ctypes.byref(desc),
-                                      float(scale), u.data_ptr(), l.data_ptr(), m.data_ptr(), _stream(q))
+                                      float(scale), u.data_ptr(), l.data_ptr(), m.data_ptr(), ws_ptr, ws_len,
+                                      _stream(q))
     _check(lib, st, "attention_chunk_stats")
     return u, l, m
 

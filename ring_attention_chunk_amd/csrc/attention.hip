@@ -1455,13 +1455,17 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
   write_rows<DP, MODE>(p, wk, o, l_run, m_ref, m_max, h);
 }
 
-// Merge of the key-range partials of each row, in range order, then u / l.
+// Merge of the key-range partials of each row, in range order, then u / l and
+// lse (ring call), or, with STATS, the merged statistics themselves: u and l
+// relative to the row's overall maximum, written to out and lse, and that
+// maximum in score units to mout (chunk-statistics call).
 // Each row is handled by LPR lanes of one wave; with VEC4 (head_dim a multiple
 // of 4) each lane reads and writes 16-byte column groups.
-template <bool VEC4>
+template <bool VEC4, bool STATS>
 __global__ __launch_bounds__(256) void combine_kernel(int64_t rows, int d, int nsplit, int lpr, int lpr_shift,
                                                       const float* __restrict__ part, float* __restrict__ out,
-                                                      float* __restrict__ lse, float c2, float scale) {
+                                                      float* __restrict__ lse, float* __restrict__ mout, float c2,
+                                                      float scale) {
   const int64_t r = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> lpr_shift;
   if (r >= rows) return;
   const int sub = threadIdx.x & (lpr - 1);
@@ -1483,13 +1487,13 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t rows, int d, int n
         u += ((const f32x4*)(part + ((int64_t)s * rows + r) * d))[c] * w;
       }
       l = lc;  // lane 0 of the row always has column group 0
-      const float inv = (lc > 0.f) ? 1.f / lc : 0.f;
+      const float inv = STATS ? 1.f : ((lc > 0.f) ? 1.f / lc : 0.f);
       ((f32x4*)(out + r * d))[c] = u * inv;
     }
   } else {
     for (int s = 0; s < nsplit; ++s)
       l = fmaf(pl[(int64_t)s * rows + r], __builtin_amdgcn_exp2f(pm[(int64_t)s * rows + r] * c2 - ms), l);
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const float inv = STATS ? 1.f : ((l > 0.f) ? 1.f / l : 0.f);
     for (int c = sub; c < d; c += lpr) {
       float u = 0.f;
       for (int s = 0; s < nsplit; ++s)
@@ -1498,7 +1502,35 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t rows, int d, int n
       out[r * d + c] = u * inv;
     }
   }
-  if (sub == 0 && lse != nullptr) lse[r] = (l > 0.f) ? mx * scale + logf(l) : -INFINITY;
+  if (sub == 0) {
+    if (STATS) {
+      lse[r] = l;
+      mout[r] = (mx == -INFINITY) ? -INFINITY : mx * scale;
+    } else if (lse != nullptr) {
+      lse[r] = (l > 0.f) ? mx * scale + logf(l) : -INFINITY;
+    }
+  }
+}
+
+// Launch of combine_kernel over `rows` rows of head_dim d.
+template <bool STATS>
+hipError_t launch_combine(int64_t rows, int d, int nsplit, const float* part, float* out, float* lse, float* mout,
+                          float c2, float scale, hipStream_t s) {
+  const bool vec4 = d % 4 == 0 && (uintptr_t)out % 16 == 0;  // partials are 256-byte aligned
+  const int cols = vec4 ? d / 4 : d;
+  int lpr = 1, sh = 0;
+  while (lpr < cols && lpr < 64) {
+    lpr <<= 1;
+    ++sh;
+  }
+  const int64_t cblocks = (rows * lpr + 255) / 256;
+  if (vec4)
+    hipLaunchKernelGGL((combine_kernel<true, STATS>), dim3((unsigned)cblocks), dim3(256), 0, s, rows, d, nsplit, lpr,
+                       sh, part, out, lse, mout, c2, scale);
+  else
+    hipLaunchKernelGGL((combine_kernel<false, STATS>), dim3((unsigned)cblocks), dim3(256), 0, s, rows, d, nsplit,
+                       lpr, sh, part, out, lse, mout, c2, scale);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1820,9 +1852,19 @@ int ra_kernel_timer_read(float* total_ms, int* count) {
   return RA_OK;
 }
 
+size_t ra_chunk_stats_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t chunk_len) {
+  if (batch <= 0 || q_heads <= 0 || head_dim <= 0 || q_len <= 0 || chunk_len <= 0) return 0;
+  // both kernels take 128 query rows per workgroup in this mode. The keys are cut only while the
+  // rows leave CUs idle: with one workgroup per CU already, the partial writes and the merge cost
+  // more than a second workgroup per CU gains (measured on 4096 rows x 4096 keys x 8 heads)
+  const int64_t base = ((q_len + BM - 1) / BM) * (int64_t)q_heads * batch;
+  const int ns = choose_nsplit(base, chunk_len, 1, 1);
+  return partial_bytes(ns, (int64_t)batch * q_heads * q_len, head_dim);
+}
+
 int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
                              int64_t q_len, const ra_kv_chunk* chunk, float scale, float* u, float* l, float* m,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   int st = check_dims(dtype, batch, q_heads, kv_heads, head_dim);
   if (st) return st;
@@ -1839,7 +1881,16 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   const bool pipe = pipe_ok(dtype, head_dim, vec, chunk, 1, false, &kps);
   const int bm = pipe ? pipe_bm(kStats) : BM;
   const int64_t n_qt = (q_len + bm - 1) / bm;
-  const int64_t nblocks = n_qt * q_heads * batch;
+  const int64_t base_blocks = n_qt * q_heads * batch;
+  // with a workspace, a grid too small for the chip is filled by cutting the keys into ranges whose
+  // partial statistics are merged afterwards (the cut depends only on the chunk's length)
+  const size_t need = ra_chunk_stats_workspace_bytes(batch, q_heads, head_dim, q_len, chunk->len);
+  if (workspace && (uintptr_t)workspace % 256 != 0)
+    return fail(RA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const int nsplit = (need > 0 && workspace && workspace_bytes >= need)
+                         ? choose_nsplit(base_blocks, chunk->len, 1, 1)
+                         : 1;
+  const int64_t nblocks = base_blocks * nsplit;
   if (nblocks > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
 
   Params p = {};
@@ -1847,6 +1898,7 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.o = u;
   p.l = l;
   p.m = m;
+  p.part = nsplit > 1 ? (float*)workspace : nullptr;
   p.one.k = chunk->k;
   p.one.v = chunk->v;
   p.one.start = 0;
@@ -1865,7 +1917,7 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   p.Hkv = kv_heads;
   p.d = head_dim;
   p.n_qt = (int)n_qt;
-  p.nsplit = 1;
+  p.nsplit = nsplit;
   p.vec = vec;
   p.kps = kps;
   p.kinv = 1.0 / kps;
@@ -1876,6 +1928,11 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   hipError_t e = launch(kStats, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, (hipStream_t)stream);
   timer_end((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention_chunk_stats launch");
+  if (nsplit > 1) {
+    e = launch_combine<true>((int64_t)batch * q_heads * q_len, head_dim, nsplit, (const float*)p.part, u, l, m, p.c2,
+                             scale, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention_chunk_stats combine launch");
+  }
   return RA_OK;
 }
 
@@ -2017,21 +2074,7 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   timer_end(hs);
   if (e != hipSuccess) return hip_fail(e, "ring_attention launch");
   if (nsplit > 1) {
-    const bool vec4 = head_dim % 4 == 0 && (uintptr_t)out % 16 == 0;  // partials are 256-byte aligned
-    const int cols = vec4 ? head_dim / 4 : head_dim;
-    int lpr = 1, sh = 0;
-    while (lpr < cols && lpr < 64) {
-      lpr <<= 1;
-      ++sh;
-    }
-    const int64_t cblocks = (rows * lpr + 255) / 256;
-    if (vec4)
-      hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)cblocks), dim3(256), 0, hs, rows, head_dim, nsplit,
-                         lpr, sh, (const float*)p.part, out, lse, p.c2, scale);
-    else
-      hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)cblocks), dim3(256), 0, hs, rows, head_dim, nsplit,
-                         lpr, sh, (const float*)p.part, out, lse, p.c2, scale);
-    e = hipGetLastError();
+    e = launch_combine<false>(rows, head_dim, nsplit, (const float*)p.part, out, lse, nullptr, p.c2, scale, hs);
     if (e != hipSuccess) return hip_fail(e, "ring_attention combine launch");
   }
   return RA_OK;

@@ -121,10 +121,16 @@ def test_empty_work_is_a_no_op(lib):
 
 def test_stats_and_merge_validation(lib):
     ch = api.KVChunk(FAKE, FAKE, 8, 0, 0, 0, 64)
-    assert lib.ra_attention_chunk_stats(1, 1, 2, 2, 64, FAKE, 4, None, 0.1, FAKE, FAKE, FAKE, None) == 1
-    assert lib.ra_attention_chunk_stats(1, 1, 2, 2, 64, FAKE, -1, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, None) == 2
-    assert lib.ra_attention_chunk_stats(1, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, None, FAKE, FAKE, None) == 1
-    assert lib.ra_attention_chunk_stats(2, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, None) == 3
+    st = lib.ra_attention_chunk_stats
+    assert st(1, 1, 2, 2, 64, FAKE, 4, None, 0.1, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert st(1, 1, 2, 2, 64, FAKE, -1, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, None, 0, None) == 2
+    assert st(1, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, None, FAKE, FAKE, None, 0, None) == 1
+    assert st(2, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, None, 0, None) == 3
+    assert st(1, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1010), 1 << 20,
+              None) == 6  # misaligned workspace
+    # a short query share against a long chunk gets room for key-range partials; a large one none
+    assert lib.ra_chunk_stats_workspace_bytes(1, 8, 64, 1024, 4096) >= 2 * 8 * 1024 * 66 * 4
+    assert lib.ra_chunk_stats_workspace_bytes(1, 8, 64, 4096, 4096) == 0  # one workgroup per CU already
     assert lib.ra_merge_chunk_stats(-1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert lib.ra_merge_chunk_stats(5, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert lib.ra_merge_chunk_stats(5, 8, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1

@@ -181,6 +181,27 @@ def test_chunk_stats_small(dtype, d):
     assert np.abs(np.log(_np(l)) + _np(m) - (np.log(rl) + rm)).max() <= (F32_TOL if dtype == "f32" else 1e-2)
 
 
+@pytest.mark.parametrize("dtype,d,nk", [("bf16", 64, 4096), ("bf16", 128, 4096), ("f32", 32, 2048)])
+def test_chunk_stats_key_range_split(dtype, d, nk):
+    """Few query rows against a long chunk: the keys are cut into ranges and the partial statistics
+    merged; the result matches the oracle and, to rounding, the uncut call."""
+    _say(f"chunk_stats split {dtype} d={d} keys={nk}")
+    w = wl.custom("stsplit", dtype, 1, 2, 2, d, [(0, 256)], [(0, nk)], False, seed=d + nk)
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    assert ra.api.load_library().ra_chunk_stats_workspace_bytes(1, 2, d, 256, nk) > 0
+    u, l, m = ra.attention_chunk_stats(q, kc[0], vc[0])
+    u0, l0, m0 = ra.attention_chunk_stats(q, kc[0], vc[0], workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    ru, rl, rm = oracle.chunk_stats(q.cpu(), kc[0].cpu(), vc[0].cpu(), 1 / math.sqrt(d))
+    _check(_np(u) / _np(l)[..., None], ru / rl[..., None], dtype)
+    tol = F32_TOL if dtype == "f32" else 1e-2
+    assert np.abs(np.log(_np(l)) + _np(m) - (np.log(rl) + rm)).max() <= tol
+    assert np.abs(_np(m) - rm).max() <= (F32_TOL if dtype == "f32" else 1e-4) * max(1, np.abs(rm).max())
+    # the same statistics as the uncut call, up to rounding
+    assert torch.equal(m, m0)
+    assert np.abs(_np(u) / _np(l)[..., None] - _np(u0) / _np(l0)[..., None]).max() <= tol
+
+
 def test_merge_random_statistics():
     _say("merge random")
     g = torch.Generator().manual_seed(3)
