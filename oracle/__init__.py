@@ -27,7 +27,11 @@ Two independent statements of what the method computes live here:
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against the pages' worked example, closed forms, brute force on tiny inputs
-and a library special case; no function is "parity unpinned".
+and a library special case. ``attention_rows`` (the same definition on
+selected rows, the reference of the full-size GPU checks) is pinned row for
+row against ``attention`` on GQA, causal, paired early/late and striped
+shares, with planted bookkeeping mistakes that the pin must catch
+(``tests/test_oracle_rows.py``). No function is "parity unpinned".
 """
 
 from .backward import attention_backward
