@@ -12,7 +12,11 @@
  * --------------------------------
  *  - All pointers to tensors are DEVICE pointers owned by the caller. The
  *    library allocates no device memory. Host pointers (descriptor arrays)
- *    need to stay valid only for the duration of the call.
+ *    need to stay valid only for the duration of the call: the descriptor
+ *    tables reach the device as kernel arguments of small copy kernels,
+ *    which the runtime captures when each launch is enqueued, so nothing
+ *    reads host memory after a call returns (no host-to-device memcpy, no
+ *    pinned staging).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
  *    default stream). A status of RA_OK means the work was enqueued; faults
  *    inside kernels surface at the caller's next synchronisation.
@@ -163,12 +167,13 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
                       void* stream);
 
 /* Device workspace, in bytes, that ra_ring_attention_backward needs: the
- * chunk table, the query and key positions (4 bytes per query row and per
- * key), per-32-row position bounds, delta (fp32 per (batch, head, query)
- * row) and, when the query rows alone cannot fill the GPU, fp32 partial dq of
- * up to 8 key ranges. A multiple of 256. */
+ * chunk and query segment tables, the query and key positions (4 bytes per
+ * query row and per key, built on the device), per-32-row position bounds,
+ * delta (fp32 per (batch, head, query) row) and, when the query rows alone
+ * cannot fill the GPU, fp32 partial dq of up to 8 key ranges. A multiple of
+ * 256. */
 size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys,
-                                        int n_chunks);
+                                        int n_chunks, int n_q_segments);
 
 /* Gradients of ring_attention for this device's share.
  * "Ring Attention: Distributed Reads with Online Softmax", section "Backward
@@ -196,7 +201,7 @@ size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int head_dim, in
  *              is the slice of its keys. Every row is written, zero for keys
  *              no local query sees.
  *  workspace   >= ra_ring_backward_workspace_bytes(...) bytes, 256-byte
- *              aligned; tables are copied there on `stream`.
+ *              aligned; tables are written there on `stream`.
  * Outputs must not overlap inputs. The result is bit-identical from run to
  * run (no atomics; every sum in a fixed order). */
 int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, int head_dim,

@@ -85,7 +85,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_ring_attention.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                       ctypes.POINTER(KVChunk), i32, i32, f32, vp, sz, vp, vp, vp]
     lib.ra_ring_attention.restype = i32
-    lib.ra_ring_backward_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32]
+    lib.ra_ring_backward_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32, i32]
     lib.ra_ring_backward_workspace_bytes.restype = sz
     lib.ra_ring_attention_backward.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                                ctypes.POINTER(KVChunk), i32, i32, f32, vp, vp, vp, vp, sz, vp, vp,
@@ -214,7 +214,8 @@ def merge_chunk_stats(acc, chunk, inplace: bool = False):
     if tuple(au.shape[:-1]) != tuple(al.shape):
         raise RingAttentionError("u must be l's shape plus a trailing head_dim axis")
     if not inplace:
-        au, al, am = au.clone(), al.clone(), am.clone()
+        # fresh row-major copies: the kernel reads and writes u as [rows, head_dim]
+        au, al, am = (t.clone(memory_format=_torch().contiguous_format) for t in (au, al, am))
     elif not (au.is_contiguous() and al.is_contiguous() and am.is_contiguous()):
         raise RingAttentionError("in-place merge needs contiguous accumulator tensors")
     bu, bl, bm = bu.contiguous(), bl.contiguous(), bm.contiguous()
@@ -251,11 +252,11 @@ def workspace_bytes(query_shape, key_lengths, n_q_segments: int = 1) -> int:
                                                       n_q_segments))
 
 
-def backward_workspace_bytes(query_shape, key_lengths) -> int:
+def backward_workspace_bytes(query_shape, key_lengths, n_q_segments: int = 1) -> int:
     """Bytes of device workspace ``ring_attention_backward`` needs for this shape."""
     B, Hq, Lq, d = query_shape
     return int(load_library().ra_ring_backward_workspace_bytes(B, Hq, d, Lq, int(sum(key_lengths)),
-                                                               len(key_lengths)))
+                                                               len(key_lengths), n_q_segments))
 
 
 def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global_offset: QOffset = 0,
@@ -364,7 +365,7 @@ def ring_attention_backward(query, key_chunks: Sequence, value_chunks: Sequence,
         scale = 1.0 / math.sqrt(d)
     lens = [int(k.shape[2]) for k in key_chunks]
     total = sum(lens)
-    need = lib.ra_ring_backward_workspace_bytes(B, Hq, d, Lq, total, n)
+    need = lib.ra_ring_backward_workspace_bytes(B, Hq, d, Lq, total, n, nseg)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace.numel() < need or workspace.data_ptr() % 256 != 0:

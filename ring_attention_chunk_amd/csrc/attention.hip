@@ -1651,6 +1651,15 @@ using namespace ra_host;
 
 int dp_of(int head_dim) { return head_dim <= 32 ? 32 : (head_dim <= 64 ? 64 : 128); }
 
+// The forward kernels' tile walk keeps a chunk's row stride (in elements) in
+// 32 bits.
+int check_row_stride(const ra_kv_chunk& c, int idx) {
+  if (c.len > 0 && c.stride_s > 0x7fffffffLL)
+    return fail(RA_ERR_UNSUPPORTED, "chunk %d: row stride %lld elements is 2^31 or more", idx,
+                (long long)c.stride_s);
+  return RA_OK;
+}
+
 // Key-range split for grids that cannot fill the chip: depends only on the
 // shape (never on the chunk list), so every split of a sequence into chunks
 // runs the same arithmetic.
@@ -1804,6 +1813,31 @@ size_t ra_ring_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_l
 // call (not around the key-range combine), and around the two gradient
 // kernels of each ring_attention_backward call, while enabled.
 namespace ra_host {
+
+// Descriptor tables travel to the device as kernel arguments: 2 KB per launch,
+// well inside the kernel argument space.
+constexpr int kUploadWords = 512;
+struct UploadArgs {
+  uint32_t w[kUploadWords];
+};
+
+__global__ __launch_bounds__(256) void upload_kernel(uint32_t* __restrict__ dst, int n, UploadArgs a) {
+  for (int i = threadIdx.x; i < n; i += 256) dst[i] = a.w[i];
+}
+
+hipError_t upload_table(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  for (size_t w0 = 0; w0 < words; w0 += kUploadWords) {
+    const int n = (int)(words - w0 < (size_t)kUploadWords ? words - w0 : (size_t)kUploadWords);
+    UploadArgs a;
+    memcpy(a.w, (const uint32_t*)src + w0, (size_t)n * 4);
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, (uint32_t*)dst + w0, n, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 constexpr int kTimerSlots = 512;
 hipEvent_t g_tev[2][kTimerSlots];
 bool g_tev_made = false;
@@ -1873,6 +1907,7 @@ int ra_attention_chunk_stats(int dtype, int batch, int q_heads, int kv_heads, in
   if (!(scale > 0.f) || !isfinite(scale)) return fail(RA_ERR_SHAPE, "scale must be finite and > 0");
   const int64_t elem = dtype == RA_BF16 ? 2 : 4;
   if ((st = check_chunk(*chunk, 0, head_dim))) return st;
+  if ((st = check_row_stride(*chunk, 0))) return st;
   if (q_len == 0 || batch == 0) return RA_OK;
   if (!q || !u || !l || !m) return fail(RA_ERR_NULL, "q, u, l and m must be non-null");
   if (chunk->len > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "chunk longer than 2^31-2 keys");
@@ -1989,6 +2024,7 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   bool vec = true;
   for (int c = 0; c < n_chunks; ++c) {
     if ((st = check_chunk(chunks[c], c, head_dim))) return st;
+    if ((st = check_row_stride(chunks[c], c))) return st;
     lk += chunks[c].len;
     vec = vec && chunk_vec_ok(chunks[c], head_dim, elem);
   }
@@ -2041,9 +2077,9 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
     row0 += q_segments[s].len;
   }
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(workspace, host, tbytes, hipMemcpyHostToDevice, hs);
+  hipError_t e = upload_table(workspace, host, tbytes, hs);
   free(host);
-  if (e != hipSuccess) return hip_fail(e, "ring_attention descriptor copy");
+  if (e != hipSuccess) return hip_fail(e, "ring_attention descriptor upload");
 
   Params p = {};
   p.q = q;

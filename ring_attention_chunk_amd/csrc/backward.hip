@@ -561,6 +561,61 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(int64_t n4, int ns, cons
 }
 
 // ---------------------------------------------------------------------------
+// Position tables of a call, built on the device from the chunk and query
+// segment descriptors: the global position of every query row and key (or the
+// "sees everything" values without a causal mask), and the smallest and largest
+// position of every 32-row query block and 32-key tile. Thread t < nqb builds
+// query block t, thread nqb + u builds key tile u.
+
+struct BwdSeg {
+  int64_t row0, len, pos0, ps;
+};
+
+__global__ __launch_bounds__(256) void bwd_positions_kernel(const BwdChunk* __restrict__ chunks, int n_chunks,
+                                                            const BwdSeg* __restrict__ segs, int n_segs,
+                                                            int64_t lq, int64_t lk, int causal, int* __restrict__ qpos,
+                                                            int* __restrict__ kpos, int* __restrict__ qblk,
+                                                            int* __restrict__ ktile) {
+  const int64_t nqb = (lq + kRows - 1) / kRows, nkt = (lk + kRows - 1) / kRows;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < nqb) {
+    const int64_t i0 = t * kRows, i1 = min(lq, i0 + kRows);
+    int s = 0;
+    while (s + 1 < n_segs && i0 >= segs[s].row0 + segs[s].len) ++s;
+    int mn = kPosMax, mx = kPosMinQ;
+    for (int64_t i = i0; i < i1; ++i) {
+      while (s + 1 < n_segs && i >= segs[s].row0 + segs[s].len) ++s;
+      const int pos = causal ? (int)(segs[s].pos0 + segs[s].ps * (i - segs[s].row0)) : kPosAllQ;
+      qpos[i] = pos;
+      mn = min(mn, pos);
+      mx = max(mx, pos);
+    }
+    qblk[2 * t] = mn;
+    qblk[2 * t + 1] = mx;
+  } else if (t < nqb + nkt) {
+    const int64_t u = t - nqb;
+    const int64_t j0 = u * kRows, j1 = min(lk, j0 + kRows);
+    // last chunk starting at or before key j0 (chunks are non-empty and in list order)
+    int lo = 0, hi = n_chunks - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (chunks[mid].start <= j0) lo = mid; else hi = mid - 1;
+    }
+    int c = lo;
+    int mn = kPosMax, mx = kPosMinQ;
+    for (int64_t j = j0; j < j1; ++j) {
+      while (c + 1 < n_chunks && j >= chunks[c].start + chunks[c].len) ++c;
+      const int pos = causal ? (int)(chunks[c].pos0 + (int64_t)chunks[c].ps * (j - chunks[c].start)) : 0;
+      kpos[j] = pos;
+      mn = min(mn, pos);
+      mx = max(mx, pos);
+    }
+    ktile[2 * u] = mn;
+    ktile[2 * u + 1] = mx;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 using namespace ra_host;
@@ -568,7 +623,7 @@ using namespace ra_host;
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t chunks, qpos, kpos, qblk, ktile, table_end, delta, part, total;
+  size_t chunks, segs, qpos, kpos, qblk, ktile, table_end, delta, part, total;
   int dq_split;
 };
 
@@ -582,11 +637,13 @@ int choose_dq_split(int batch, int q_heads, int64_t q_len, int64_t total_keys) {
   return ns;
 }
 
-BwdLayout bwd_layout(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys, int n_chunks) {
+BwdLayout bwd_layout(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys, int n_chunks,
+                     int n_q_segments) {
   BwdLayout L;
   const int64_t nqb = (q_len + kRows - 1) / kRows, nkt = (total_keys + kRows - 1) / kRows;
   L.chunks = 0;
-  L.qpos = L.chunks + al256(sizeof(BwdChunk) * (size_t)(n_chunks > 0 ? n_chunks : 1));
+  L.segs = L.chunks + al256(sizeof(BwdChunk) * (size_t)(n_chunks > 0 ? n_chunks : 1));
+  L.qpos = L.segs + al256(sizeof(BwdSeg) * (size_t)(n_q_segments > 0 ? n_q_segments : 1));
   L.kpos = L.qpos + al256(sizeof(int) * (size_t)(q_len > 0 ? q_len : 1));
   L.qblk = L.kpos + al256(sizeof(int) * (size_t)(total_keys > 0 ? total_keys : 1));
   L.ktile = L.qblk + al256(2 * sizeof(int) * (size_t)(nqb > 0 ? nqb : 1));
@@ -629,11 +686,12 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
 extern "C" {
 
 size_t ra_ring_backward_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys,
-                                        int n_chunks) {
+                                        int n_chunks, int n_q_segments) {
   if (n_chunks < 0) n_chunks = 0;
+  if (n_q_segments < 0) n_q_segments = 0;
   if (q_len < 0) q_len = 0;
   if (total_keys < 0) total_keys = 0;
-  return bwd_layout(batch, q_heads, head_dim, q_len, total_keys, n_chunks).total;
+  return bwd_layout(batch, q_heads, head_dim, q_len, total_keys, n_chunks, n_q_segments).total;
 }
 
 int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
@@ -676,19 +734,19 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
   const int64_t blocks_q = ((lq + kGroupRows - 1) / kGroupRows) * batch * q_heads;
   const int64_t blocks_k = ((lk + kGroupRows - 1) / kGroupRows) * batch * kv_heads;
   if (blocks_q > 0x7fffffffLL || blocks_k > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
-  const BwdLayout L = bwd_layout(batch, q_heads, head_dim, lq, lk, n_chunks);
+  const BwdLayout L = bwd_layout(batch, q_heads, head_dim, lq, lk, n_chunks, n_q_segments);
   if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % 256 != 0)
     return fail(RA_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);
 
-  // host tables: chunk descriptors, query and key positions, per-block bounds
-  char* host = (char*)calloc(1, L.table_end);
+  // Chunk and query-segment descriptors go to the workspace as kernel arguments
+  // (host memory is read only during this call); the position tables are then
+  // built from them on the device.
+  const size_t dbytes = L.qpos;  // chunk table, then segment table
+  char* host = (char*)calloc(1, dbytes);
   if (!host) return fail(RA_ERR_UNSUPPORTED, "host allocation failed");
   BwdChunk* hc = (BwdChunk*)(host + L.chunks);
-  int* hqp = (int*)(host + L.qpos);
-  int* hkp = (int*)(host + L.kpos);
-  int* hqb = (int*)(host + L.qblk);
-  int* hkt = (int*)(host + L.ktile);
+  BwdSeg* hs_ = (BwdSeg*)(host + L.segs);
   int nc = 0;
   int64_t start = 0;
   for (int c = 0; c < n_chunks; ++c) {
@@ -704,36 +762,30 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
     d.ss = ch.stride_s;
     d.pos0 = (int32_t)ch.global_offset;
     d.ps = (int32_t)pos_step(ch.pos_stride);
-    for (int64_t i = 0; i < ch.len; ++i) hkp[start + i] = causal ? (int)(ch.global_offset + d.ps * i) : 0;
     start += ch.len;
   }
-  int64_t row = 0;
+  int64_t row0 = 0;
   for (int s = 0; s < n_q_segments; ++s) {
-    const ra_q_segment& g = q_segments[s];
-    for (int64_t i = 0; i < g.len; ++i)
-      hqp[row + i] = causal ? (int)(g.global_offset + pos_step(g.pos_stride) * i) : kPosAllQ;
-    row += g.len;
-  }
-  for (int64_t qb = 0; qb * kRows < lq; ++qb) {
-    int mx = kPosMinQ;
-    for (int64_t i = qb * kRows; i < lq && i < (qb + 1) * kRows; ++i) mx = hqp[i] > mx ? hqp[i] : mx;
-    int mn = kPosMax;
-    for (int64_t i = qb * kRows; i < lq && i < (qb + 1) * kRows; ++i) mn = hqp[i] < mn ? hqp[i] : mn;
-    hqb[2 * qb] = mn;
-    hqb[2 * qb + 1] = mx;
-  }
-  for (int64_t t = 0; t * kRows < lk; ++t) {
-    int mn = kPosMax;
-    for (int64_t j = t * kRows; j < lk && j < (t + 1) * kRows; ++j) mn = hkp[j] < mn ? hkp[j] : mn;
-    int mx = kPosMinQ;
-    for (int64_t j = t * kRows; j < lk && j < (t + 1) * kRows; ++j) mx = hkp[j] > mx ? hkp[j] : mx;
-    hkt[2 * t] = mn;
-    hkt[2 * t + 1] = mx;
+    hs_[s].row0 = row0;
+    hs_[s].len = q_segments[s].len;
+    hs_[s].pos0 = q_segments[s].global_offset;
+    hs_[s].ps = pos_step(q_segments[s].pos_stride);
+    row0 += q_segments[s].len;
   }
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(workspace, host, L.table_end, hipMemcpyHostToDevice, hs);
+  hipError_t e = upload_table(workspace, host, dbytes, hs);
   free(host);
-  if (e != hipSuccess) return hip_fail(e, "ring_attention_backward table copy");
+  if (e != hipSuccess) return hip_fail(e, "ring_attention_backward descriptor upload");
+  {
+    char* ws = (char*)workspace;
+    const int64_t nthreads = (lq + kRows - 1) / kRows + (lk + kRows - 1) / kRows;
+    hipLaunchKernelGGL(bwd_positions_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, hs,
+                       (const BwdChunk*)(ws + L.chunks), nc, (const BwdSeg*)(ws + L.segs), n_q_segments, lq, lk,
+                       causal ? 1 : 0, (int*)(ws + L.qpos), (int*)(ws + L.kpos), (int*)(ws + L.qblk),
+                       (int*)(ws + L.ktile));
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "ring_attention_backward position tables launch");
+  }
 
   BwdParams p = {};
   char* ws = (char*)workspace;

@@ -36,6 +36,13 @@ bool chunk_vec_ok(const ra_kv_chunk& c, int head_dim, int64_t elem);
 void timer_begin(hipStream_t s);
 void timer_end(hipStream_t s);
 
+// Stream-ordered copy of `bytes` (a multiple of 4) of host memory to device
+// memory at `dst`, carried as kernel arguments of small copy kernels: the
+// runtime captures arguments when a launch is enqueued, so the host bytes need
+// to stay valid only for this call, and no host-to-device copy engine or
+// staging buffer is involved. Meant for descriptor tables of a few KB.
+hipError_t upload_table(void* dst, const void* src, size_t bytes, hipStream_t s);
+
 }  // namespace ra_host
 
 #endif  // RA_HOST_COMMON_H

@@ -106,6 +106,12 @@ def test_ring_validation_codes(lib):
     seg = (api.QSegment * 1)(api.QSegment(4, 3, 1 << 30))
     assert _ring(lib, segs=seg, causal=1) == 2
     assert _ring(lib, out=None) == 1
+    # the forward kernels keep a chunk's row stride in 32 bits: 2^31 elements or more is refused
+    bad = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 8, 0, 0, 0, 1 << 31))
+    assert _ring(lib, chunks=bad) == 4
+    assert b"row stride" in lib.ra_last_error()
+    ok = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 8, 0, 0, 0, (1 << 31) - 1))
+    assert _ring(lib, chunks=ok) == 6  # accepted; fails later, on the missing workspace
     assert _ring(lib, ws=None, wsb=0) == 6
     assert _ring(lib, ws=ctypes.c_void_p(0x1010), wsb=1 << 20) == 6  # misaligned
     assert b"workspace" in lib.ra_last_error()
@@ -126,6 +132,8 @@ def test_stats_and_merge_validation(lib):
     assert st(1, 1, 2, 2, 64, FAKE, -1, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, None, 0, None) == 2
     assert st(1, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, None, FAKE, FAKE, None, 0, None) == 1
     assert st(2, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, None, 0, None) == 3
+    wide = api.KVChunk(FAKE, FAKE, 8, 0, 0, 0, 1 << 32)
+    assert st(1, 1, 2, 2, 64, FAKE, 4, ctypes.byref(wide), 0.1, FAKE, FAKE, FAKE, None, 0, None) == 4
     assert st(1, 1, 2, 2, 64, FAKE, 4, ctypes.byref(ch), 0.1, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1010), 1 << 20,
               None) == 6  # misaligned workspace
     # a short query share against a long chunk gets room for key-range partials; a large one none
@@ -164,10 +172,10 @@ def test_backward_validation_codes(lib):
     assert bwd(dq=None) == 1
     assert bwd() == 6  # no workspace
     assert b"workspace" in lib.ra_last_error()
-    need = lib.ra_ring_backward_workspace_bytes(1, 2, 64, 4, 8, 1)
+    need = lib.ra_ring_backward_workspace_bytes(1, 2, 64, 4, 8, 1, 1)
     assert need % 256 == 0 and need >= 4 * (4 + 8) + 4 * 2 * 4
     # a short share with many keys gets room for partial dq of several key ranges
-    small = lib.ra_ring_backward_workspace_bytes(1, 8, 64, 4096, 32768, 8)
+    small = lib.ra_ring_backward_workspace_bytes(1, 8, 64, 4096, 32768, 8, 1)
     assert small >= 2 * 8 * 4096 * 64 * 4
-    big = lib.ra_ring_backward_workspace_bytes(1, 32, 128, 8192, 65536, 8)
+    big = lib.ra_ring_backward_workspace_bytes(1, 32, 128, 8192, 65536, 8, 2)
     assert big < 32 * 8192 * 128 * 4  # enough query rows: no partials
