@@ -3,11 +3,15 @@
 
 One step is one ``ring_attention`` call over one device's full share (every
 key/value chunk, in ring order, with the causal mask if the workload has one),
-with inputs already resident in HBM. The JSON line reports the counted
-throughput ``4 * d * Hq * (allowed query-key pairs)`` per second, the roofline
-of the attention kernel (bf16 MFMA bound), the standalone chunk-statistics and
-merge legs (the merge is HBM-bound, next to a device copy of the same size),
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+with inputs already resident in HBM. The headline is the largest share that
+fits one GPU: the long-context GQA share (16384 local queries, 8 query heads
+on one key/value head, d = 128, against 1,048,576 keys in 64 shards). The JSON
+line reports its counted throughput ``4 * d * Hq * (allowed query-key pairs)``
+per second and the roofline of its attention kernel (bf16 MFMA bound); the
+other bf16 shares, each timed the same way, in a ``configs`` block; the
+standalone chunk-statistics and merge legs (the merge is HBM-bound, next to a
+device copy of the same size) and the backward pass in ``legs``; and the fp64
+CPU oracle timed on a bounded sample of the headline share.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
 """
@@ -15,6 +19,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
 import argparse
 import hashlib
 import json
+import math
 import os
 import platform
 import sys
@@ -27,25 +32,34 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 KERNEL_SOURCE = os.path.join(ROOT, "ring_attention_chunk_amd", "csrc", "attention.hip")
+HEADLINE = 4                 # long_gqa_hq8_hkv1_d128_q16k_k1m: the largest share on one GPU
+OTHER_CONFIGS = "1,2,3,5"    # the other bf16 shares, reported in the configs block
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed calls first (default: as many as take about one second, so that the "
-                         "GPU clocks have settled under load; a cold GPU times several percent slow)")
-    ap.add_argument("--config", type=int, default=1, help="workload index (1 is the reported workload)")
+    ap.add_argument("--steps", type=int, default=20, help="timed calls of the headline share")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed calls right before the timed ones")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="untimed calls for about this long before the warm-up, so that the GPU clocks have "
+                         "settled under load (reported as clock_settle; 0 turns it off)")
+    ap.add_argument("--config", type=int, default=HEADLINE, help="workload index of the headline share")
+    ap.add_argument("--configs", default=OTHER_CONFIGS,
+                    help="comma-separated workload indices timed in the configs block ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-legs", action="store_true", help="skip the chunk-stats and merge legs")
+    ap.add_argument("--no-legs", action="store_true", help="skip the chunk-stats, merge and backward legs")
     ap.add_argument("--profile-run", action="store_true",
                     help="launch sequence for rocprofv3 counter passes: the workload's ring_attention, a device "
                          "copy of COPY_BYTES, then the merge leg; prints what was launched")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR"),
-                    help="turn the counter CSVs of the three --profile-run passes into profiles/ summaries")
-    ap.add_argument("--command", default="", help="with --summarize-pmc: the command lines that made the CSVs")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="turn the counter CSVs of the --profile-run passes (FETCH_SIZE, WRITE_SIZE, SQ, and "
+                         "optionally a second SQ pass of instruction counts) into a profiles/ summary")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_JSON"),
+                    help="turn a rocprofv3 --kernel-trace --stats run of this script and the JSON line it printed "
+                         "into a profiles/ summary")
+    ap.add_argument("--command", default="", help="with --summarize-*: the command lines that made the files")
     return ap.parse_args()
 
 
@@ -78,15 +92,26 @@ def timed(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps  # ms per call
 
 
-def settle_warmup(fn, torch, seconds=1.0, cap=5000):
-    """Number of untimed calls that take about `seconds` (at least 5), from one timed call."""
+def call_seconds(fn, torch):
+    """Wall time of one call after one untimed call."""
     fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     fn()
     torch.cuda.synchronize()
-    dt = max(time.perf_counter() - t0, 1e-6)
-    return int(min(cap, max(5, round(seconds / dt))))
+    return max(time.perf_counter() - t0, 1e-6)
+
+
+def settle(fn, torch, seconds):
+    """Untimed calls for about `seconds` (clock settling under load); returns (calls, seconds)."""
+    if seconds <= 0:
+        return 0, 0.0
+    n = int(min(5000, max(1, round(seconds / call_seconds(fn, torch)))))
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    return n + 2, round(time.perf_counter() - t0, 3)
 
 
 def timed_with_kernel(fn, steps, warmup, torch, api):
@@ -109,39 +134,6 @@ def timed_with_kernel(fn, steps, warmup, torch, api):
     return start.elapsed_time(stop) / steps, total / n
 
 
-def backward_leg(w, q, kc, vc, offs, args, torch, ra):
-    """The backward pass of the same share (dQ, and this share's dK, dV per chunk) from the forward's out
-    and lse, with a seeded bf16 upstream gradient. Counted flops: 10*d per allowed pair and query head
-    (five matrix products of 2*d: S, dP, dV, dK, dQ); the kernels recompute S and dP a second time."""
-    from ring_attention_chunk_amd import workloads as wl
-
-    dev = q.device
-    out, lse = ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
-                                 return_lse=True, kv_position_strides=w.kv_strides)
-    g = torch.Generator(device=dev).manual_seed(7)
-    dout = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
-    ws = torch.empty(ra.api.backward_workspace_bytes(tuple(q.shape), [c.shape[2] for c in kc]), dtype=torch.uint8,
-                     device=dev)
-
-    def step():
-        return ra.ring_attention_backward(q, kc, vc, out, lse, dout, w.q_runs, offs, causal=w.causal,
-                                          scale=w.softmax_scale, kv_position_strides=w.kv_strides, workspace=ws)
-
-    steps = max(5, min(args.steps, 20))
-    ms, pair_ms = timed_with_kernel(step, steps, 3, torch, ra.api)
-    kernels_ms = 2 * pair_ms  # the dK/dV kernel and the dQ kernel, each timed by its own event pair
-    flops = 10 * w.head_dim * w.q_heads * w.batch * wl.unmasked_pairs_per_head(w)
-    return {
-        "ms": round(ms, 4),
-        "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
-        "kernels_ms": round(kernels_ms, 4),
-        "kernels_TFLOP/s": round(flops / (kernels_ms * 1e-3) / 1e12, 2),
-        "frac_of_bf16_peak": round(flops / (kernels_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-        "counted_flops": flops,
-        "shape": f"{w.name}: dq, and dk, dv of every chunk; bf16 dout",
-    }
-
-
 def dominant_kernel(w):
     """Name of the kernel that does a workload's attention: every bf16 workload here (aligned rows,
     whole 16-byte pieces) runs the pipelined bf16 kernel, fp32 the general one."""
@@ -160,47 +152,252 @@ def traffic_for(w):
     return t.get("bytes_per_launch")
 
 
+def measure_share(w, steps, warmup, settle_s, torch, ra, wl, dev="cuda:0"):
+    """Time ``ring_attention`` over share ``w``: settle, warm up, then ``steps`` timed calls.
+
+    Returns the entry of the JSON line and the device inputs (for the legs and the CPU baseline)."""
+    q, k, v, kc, vc = wl.generate_torch(w, dev)
+    offs = w.kv_offsets
+    ws = torch.empty(ra.api.workspace_bytes(tuple(q.shape), [c.shape[2] for c in kc], len(w.q_segments)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
+                                 workspace=ws, kv_position_strides=w.kv_strides)
+
+    if steps is None:  # configs block: enough calls for about 0.3 s of timed work
+        steps = int(min(500, max(10, math.ceil(0.3 / call_seconds(step, torch)))))
+    settle_calls, settle_sec = settle(step, torch, settle_s)
+    ms, kernel_ms = timed_with_kernel(step, steps, warmup, torch, ra.api)
+    flops = wl.counted_flops(w)
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
+    entry = {
+        "ms": round(ms, 4),
+        "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+        "kernel_ms": round(kernel_ms, 4),
+        "kernel_TFLOP/s": round(kernel_tflops, 2),
+        "frac": round(kernel_tflops / peak, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "clock_settle_calls": settle_calls,
+        "counted_flops": flops,
+    }
+    return entry, (q, kc, vc, offs)
+
+
+def describe(w):
+    return {
+        "workload": w.name,
+        "batch": w.batch,
+        "q_heads": w.q_heads,
+        "kv_heads": w.kv_heads,
+        "head_dim": w.head_dim,
+        "local_queries": w.lq,
+        "keys": w.lk,
+        "kv_chunks": len(w.chunks),
+        "causal": w.causal,
+        "pos_stride": w.pos_stride,
+    }
+
+
+def backward_leg(w, q, kc, vc, offs, args, torch, ra):
+    """The backward pass of the same share (dQ, and this share's dK, dV per chunk) from the forward's out
+    and lse, with a seeded bf16 upstream gradient. Counted flops: 10*d per allowed pair and query head
+    (five matrix products of 2*d: S, dP, dV, dK, dQ); the kernels recompute S and dP a second time."""
+    from ring_attention_chunk_amd import workloads as wl
+
+    dev = q.device
+    out, lse = ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
+                                 return_lse=True, kv_position_strides=w.kv_strides)
+    g = torch.Generator(device=dev).manual_seed(7)
+    dout = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
+    ws = torch.empty(ra.api.backward_workspace_bytes(tuple(q.shape), [c.shape[2] for c in kc], len(w.q_segments)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return ra.ring_attention_backward(q, kc, vc, out, lse, dout, w.q_runs, offs, causal=w.causal,
+                                          scale=w.softmax_scale, kv_position_strides=w.kv_strides, workspace=ws)
+
+    steps = max(3, min(args.steps, 10))
+    ms, pair_ms = timed_with_kernel(step, steps, 2, torch, ra.api)
+    kernels_ms = 2 * pair_ms  # the dK/dV kernel and the dQ kernel, each timed by its own event pair
+    flops = 10 * w.head_dim * w.q_heads * w.batch * wl.unmasked_pairs_per_head(w)
+    return {
+        "ms": round(ms, 4),
+        "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+        "kernels_ms": round(kernels_ms, 4),
+        "kernels_TFLOP/s": round(flops / (kernels_ms * 1e-3) / 1e12, 2),
+        "frac_of_bf16_peak": round(flops / (kernels_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "counted_flops": flops,
+        "shape": f"{w.name}: dq, and dk, dv of every chunk; bf16 dout",
+    }
+
+
+def stats_leg(q, k0, v0, scale, args, torch, ra):
+    """Standalone attention_chunk_stats of one chunk (no mask): 4 * d flops per (query, key) pair."""
+    B, Hq, Lq, d = q.shape
+    steps = int(min(500, max(10, math.ceil(0.2 / call_seconds(lambda: ra.attention_chunk_stats(
+        q, k0, v0, scale=scale), torch)))))
+    ms, kernel_ms = timed_with_kernel(lambda: ra.attention_chunk_stats(q, k0, v0, scale=scale), steps, 5, torch,
+                                      ra.api)
+    flops = 4 * d * Hq * B * Lq * k0.shape[2]
+    return {"ms": round(ms, 4), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "kernel_ms": round(kernel_ms, 4), "kernel_TFLOP/s": round(flops / (kernel_ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flops / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "steps": steps, "shape": f"{Lq} queries x {k0.shape[2]} keys, {Hq} heads, d={d}"}
+
+
+def merge_leg(args, torch, ra, dev="cuda:0"):
+    """Standalone merge at the 32-head, d=128, 8192-row shape with 4 rotating buffer pairs (1.6 GB, beyond
+    the 256 MB last-level cache), next to a device copy of the same byte count."""
+    rows, d = MERGE_ROWS, MERGE_D
+    sets = [(torch.randn(rows, d, device=dev), torch.rand(rows, device=dev) + 0.5,
+             torch.randn(rows, device=dev)) for _ in range(8)]
+    it = [0]
+
+    def merge_step():
+        i = it[0]
+        it[0] = (i + 2) % 8
+        ra.merge_chunk_stats(sets[i], sets[i + 1], inplace=True)
+
+    ms_m = timed(merge_step, 200, 20, torch)
+    mbytes = 12 * (d + 2) * rows
+    srcs = [torch.empty(mbytes // 8, dtype=torch.float32, device=dev) for _ in range(3)]
+    dst = torch.empty_like(srcs[0])  # read + write = mbytes
+    ci = [0]
+
+    def copy_step():
+        j = ci[0]
+        ci[0] = (j + 1) % 3
+        dst.copy_(srcs[j])
+
+    ms_c = timed(copy_step, 200, 20, torch)
+    del sets, srcs, dst
+    return {
+        "ms": round(ms_m, 4),
+        "GB/s": round(mbytes / (ms_m * 1e-3) / 1e9, 1),
+        "bytes_per_call": mbytes,
+        "frac_of_hbm_peak": round(mbytes / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "device_copy_GB/s": round(mbytes / (ms_c * 1e-3) / 1e9, 1),
+        "shape": f"{rows} rows x d={d}, fp32, 4 rotating buffer sets",
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, q, kc, vc, offs, seconds):
-    """The fp64 oracle on host cores over whole row blocks of the same share, for ~`seconds`."""
+    """The fp64 oracle, as it stands, on the host cores of this process's affinity mask.
+
+    Tasks are blocks of query rows of one head against every key, taken head by head from the first row;
+    a pool of one thread per core runs them with single-threaded BLAS (numpy's element-wise work, such as
+    the exponentials, is single-threaded, so one task per core keeps every core busy). New tasks start
+    until ``seconds`` have passed; the tasks in flight then finish. The inputs are converted to fp64 host
+    arrays before the clock starts (input preparation, like inputs resident in HBM on the GPU side).
+    """
+    import threading
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
+
     import numpy as np
 
     import oracle
     from ring_attention_chunk_amd import workloads as wl
 
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, 32))
+    blas = {}
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            blas = {"internal_api": info[0].get("internal_api"), "version": info[0].get("version"),
+                    "library": os.path.basename(info[0].get("filepath", ""))}
+        limiter = threadpool_limits(limits=1, user_api="blas")
     except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = 1
+        limiter = None
+    group = w.q_heads // w.kv_heads
     qpos = wl.q_positions(w)
-    qh = q.cpu()
-    kh = [c.cpu() for c in kc]
-    vh = [c.cpu() for c in vc]
-    block = 256
-    flops, rows, t0 = 0, 0, time.perf_counter()
-    kpos = np.sort(wl.k_positions(w))
-    h = 0
-    r0 = 0
-    while time.perf_counter() - t0 < seconds:
+    kpos_sorted = np.sort(wl.k_positions(w))
+    block = int(max(1, min(256, (1 << 26) // max(w.lk, 1))))
+    q64 = {}
+    kv64 = {}
+    lock = threading.Lock()
+
+    def head_inputs(h):
+        with lock:
+            if h not in q64:
+                q64[h] = q[:, h:h + 1].float().cpu().double().numpy()
+            hk = h // group
+            if hk not in kv64:
+                kv64[hk] = ([c[:, hk:hk + 1].float().cpu().double().numpy() for c in kc],
+                            [c[:, hk:hk + 1].float().cpu().double().numpy() for c in vc])
+            return q64[h], kv64[hk]
+
+    tasks = [(h, r0) for h in range(w.q_heads) for r0 in range(0, w.lq, block)]
+    # inputs of the heads the budget can reach, prepared before the clock starts
+    for h in range(min(w.q_heads, 1 + (workers * block) // max(w.lq, 1))):
+        head_inputs(h)
+
+    def run(task):
+        h, r0 = task
         r1 = min(w.lq, r0 + block)
-        oracle.attention(qh[:, h:h + 1, r0:r1], [c[:, (h * w.kv_heads) // w.q_heads:][:, :1] for c in kh],
-                         [c[:, (h * w.kv_heads) // w.q_heads:][:, :1] for c in vh], qpos[r0:r1], offs,
-                         causal=w.causal, scale=w.softmax_scale, kv_strides=w.kv_strides)
-        pairs = (r1 - r0) * w.lk if not w.causal else int(np.searchsorted(kpos, qpos[r0:r1], side="right").sum())
-        flops += 4 * w.head_dim * pairs * w.batch
-        rows += (r1 - r0) * w.batch
-        r0 = r1
-        if r0 >= w.lq:
-            r0, h = 0, (h + 1) % w.q_heads
-    wall = time.perf_counter() - t0
+        qh, (kh, vh) = head_inputs(h)
+        oracle.attention(qh[:, :, r0:r1], kh, vh, qpos[r0:r1], offs, causal=w.causal, scale=w.softmax_scale,
+                         kv_strides=w.kv_strides)
+        if w.causal:
+            pairs = int(np.searchsorted(kpos_sorted, qpos[r0:r1], side="right").sum())
+        else:
+            pairs = (r1 - r0) * w.lk
+        return 4 * w.head_dim * pairs * w.batch, (r1 - r0) * w.batch, time.perf_counter()
+
+    flops = rows = 0
+    t0 = time.perf_counter()
+    t_end = t0
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        pending = set()
+        nxt = 0
+        while True:
+            # keep every worker busy until the budget is spent (at least one task runs)
+            while len(pending) < workers and nxt < len(tasks) and (nxt == 0 or time.perf_counter() - t0 < seconds):
+                pending.add(pool.submit(run, tasks[nxt]))
+                nxt += 1
+            if not pending:
+                break
+            done, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for f in done:
+                a, b, t = f.result()
+                flops, rows, t_end = flops + a, rows + b, max(t_end, t)
+    if limiter is not None:
+        limiter.restore_original_limits()
+    wall = t_end - t0
+    full = wl.counted_flops(w)
+    heads_done = sorted({h for h, _ in tasks[:nxt]})
     return {
         "value": flops / wall / 1e12,
         "unit": "TFLOP/s",
-        "cores": cores,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{rows} query rows (blocks of {block} rows, head by head, every key) of {w.name}; "
-                  f"{wall:.1f} s wall; numpy fp64 on {platform.processor() or platform.machine()}",
+        "sample": f"{rows} query rows of {w.name} ({nxt} tasks of up to {block} rows of one head, heads "
+                  f"{heads_done[0]}..{heads_done[-1]}, every key each); {wall:.1f} s wall on {workers} threads "
+                  f"with 1 BLAS thread each",
+        "affinity_cores": cores,
+        "cpu_model": _cpu_model(),
+        "numpy": np.__version__,
+        "blas": blas,
+        "rows": rows,
+        "wall_s": round(wall, 2),
+        "sample_flops": flops,
+        "extrapolated_full_config_s": round(wall * full / max(flops, 1), 1),
     }
 
 
@@ -212,8 +409,6 @@ def profile_run(args):
     from ring_attention_chunk_amd import workloads as wl
 
     dev = "cuda:0"
-    if args.warmup is None:
-        args.warmup = 1
     w = wl.config(args.config)
     q, k, v, kc, vc = wl.generate_torch(w, dev)
     offs = [o for o, _ in w.chunks]
@@ -275,7 +470,11 @@ def summarize_pmc(args):
     from ring_attention_chunk_amd import workloads as wl
 
     w = wl.config(args.config)
-    fetch, write, sq = (_counter_rows(d) for d in args.summarize_pmc)
+    dirs = args.summarize_pmc
+    if len(dirs) not in (3, 4):
+        raise SystemExit("--summarize-pmc takes the FETCH_SIZE, WRITE_SIZE and SQ directories (and optionally a "
+                         "second SQ directory of instruction counts)")
+    fetch, write, sq = (_counter_rows(d) for d in dirs[:3])
     copy_name = "neg_kernel"
     attn_name = dominant_kernel(w)
     f_copy, _ = _per_dispatch(fetch, copy_name, "FETCH_SIZE")
@@ -324,6 +523,16 @@ def summarize_pmc(args):
         "dispatches_averaged": n_attn,
         "commands": args.command,
     }
+    if len(dirs) == 4:
+        ins = _counter_rows(dirs[3])
+        valu, _ = _per_dispatch(ins, attn_name, "SQ_INSTS_VALU")
+        mfma, _ = _per_dispatch(ins, attn_name, "SQ_INSTS_MFMA")
+        lds, _ = _per_dispatch(ins, attn_name, "SQ_INSTS_LDS")
+        salu, _ = _per_dispatch(ins, attn_name, "SQ_INSTS_SALU")
+        waves, _ = _per_dispatch(ins, attn_name, "SQ_WAVES")
+        out["instructions_per_launch"] = {"SQ_INSTS_VALU": valu, "SQ_INSTS_MFMA": mfma, "SQ_INSTS_LDS": lds,
+                                          "SQ_INSTS_SALU": salu, "SQ_WAVES": waves,
+                                          "valu_per_mfma": valu / mfma if valu and mfma else None}
     path = os.path.join(ROOT, "profiles", f"{attn_name}_{w.name}_hbm_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -331,10 +540,103 @@ def summarize_pmc(args):
     print(json.dumps(out, indent=1))
 
 
+_MODES = {"0": "stats", "1": "ring full", "2": "ring causal"}
+_MASKS = {"0": "no mask", "1": "mask", "2": "strided mask"}
+
+
+def _kernel_label(name):
+    import re
+
+    m = re.search(r"attention_bf16_kernel<(\d+), (\d), (\d)>", name)
+    if m:
+        return f"attention_bf16_kernel<{m.group(1)}, {_MODES[m.group(2)]}, {_MASKS[m.group(3)]}>"
+    m = re.search(r"attention_kernel<([\w_ ]+), (\d+), (\d)>", name)
+    if m:
+        return f"attention_kernel<{m.group(1)}, {m.group(2)}, {_MODES[m.group(3)]}>"
+    m = re.search(r"(dkdv_kernel|dq_kernel)<(\d+)>", name)
+    if m:
+        return f"{m.group(1)}<{m.group(2)}>"
+    for k in ("dq_reduce_kernel", "delta_kernel", "bwd_positions_kernel", "merge_kernel", "combine_kernel",
+              "upload_kernel", "__amd_rocclr_copyBuffer"):
+        if k in name:
+            return k
+    return None
+
+
+def summarize_trace(args):
+    """Kernel-trace summary of one run of this script: this library's kernels from run_kernel_stats.csv,
+    and, for each timed share of the JSON line, its attention kernel's average against the kernel timer."""
+    import csv
+    import glob
+    import re
+
+    from ring_attention_chunk_amd import workloads as wl
+
+    tdir, jpath = args.summarize_trace
+    files = sorted(glob.glob(os.path.join(tdir, "**", "*kernel_stats.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {tdir}")
+    rows = list(csv.DictReader(open(files[0])))
+    with open(jpath) as f:
+        d = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    stats = {}
+    for r in rows:
+        lab = _kernel_label(r["Name"])
+        if lab:
+            prev = stats.get(lab)
+            calls = int(r["Calls"])
+            tot = float(r["TotalDurationNs"]) if "TotalDurationNs" in r else float(r["AverageNs"]) * calls
+            if prev:
+                calls += prev[0]
+                tot += prev[1]
+            stats[lab] = (calls, tot, min(float(r["MinNs"]), prev[2] if prev else 1e30),
+                          max(float(r["MaxNs"]), prev[3] if prev else 0.0))
+    head = d["config"]["workload"]
+    out = [f"# attention_bf16_kernel: kernel trace of the benchmark (headline {head})", "",
+           "Command (GPU box, from the repository root):", "", "```", args.command, "```", "",
+           "From `kernel_stats.csv` (this library's kernels; durations in µs):", "",
+           "| Kernel | Calls | Average µs | Min µs | Max µs |", "|---|---|---|---|---|"]
+    for lab, (calls, tot, mn, mx) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| {lab} | {calls} | {tot / calls / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} |")
+    out += ["", "Each share's attention kernel in the trace against the library's kernel timer in the same run "
+            "(the kernel variant of a share is unique to it in this run, so the trace's average is that share's "
+            "own; it includes the untimed settle and warm-up calls):", "",
+            "| Share | Kernel | Trace average µs | TFLOP/s (trace) | % of 2500 | Kernel timer µs | TFLOP/s (timer) |",
+            "|---|---|---|---|---|---|---|"]
+    shares = [(head, d["roofline"]["kernel_ms"], d["config"]["counted_flops"])]
+    for name, e in d.get("configs", {}).items():
+        shares.append((name, e["kernel_ms"], e["counted_flops"]))
+    by_name = {wl.config(i).name: wl.config(i) for i in wl.CONFIGS}
+    for name, kms, flops in shares:
+        w = by_name.get(name)
+        if w is None:
+            continue
+        mode = "2" if w.causal else "1"
+        mask = ("2" if w.pos_stride != 1 else "1") if w.causal else ("1" if w.lk % (64 if w.head_dim > 64 else 128)
+                                                                    else "0")
+        dp = 32 if w.head_dim <= 32 else (64 if w.head_dim <= 64 else 128)
+        lab = f"attention_bf16_kernel<{dp}, {_MODES[mode]}, {_MASKS[mask]}>"
+        if lab not in stats:
+            continue
+        calls, tot, _, _ = stats[lab]
+        avg = tot / calls / 1e3
+        out.append(f"| {name} | {lab} | {avg:.1f} | {flops / (avg * 1e-6) / 1e12:.0f} | "
+                   f"{100 * flops / (avg * 1e-6) / 1e12 / BF16_PEAK_TFLOPS:.1f} | {kms * 1e3:.1f} | "
+                   f"{flops / (kms * 1e-3) / 1e12:.0f} |")
+    out += ["", f"Kernel source digest {source_digest()} (sha256 of attention.hip without comments)."]
+    path = os.path.join(ROOT, "profiles", f"attention_bf16_kernel_{head}_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the whole share on a single MI355X and has no "
@@ -352,113 +654,71 @@ def main():
         return
     dev = "cuda:0"
     w = wl.config(args.config)
-    q, k, v, kc, vc = wl.generate_torch(w, dev)
-    offs = [o for o, _ in w.chunks]
-    flops = wl.counted_flops(w)
-    ws = torch.empty(ra.api.workspace_bytes(tuple(q.shape), [c.shape[2] for c in kc], len(w.q_segments)),
-                     dtype=torch.uint8, device=dev)
-
-    def step():
-        return ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
-                                 workspace=ws, kv_position_strides=w.kv_strides)
-
-    if args.warmup is None:
-        args.warmup = settle_warmup(step, torch)
-    ms, kernel_ms = timed_with_kernel(step, args.steps, args.warmup, torch, ra.api)
-    tflops = flops / (ms * 1e-3) / 1e12
-    # the roofline is the attention kernel's: its algorithmic flops per launch over its own average
-    # device time, from HIP events the library records around that launch on the call's stream
-    kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
+    entry, (q, kc, vc, offs) = measure_share(w, args.steps, args.warmup, args.settle_seconds, torch, ra, wl, dev)
+    flops = entry["counted_flops"]
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-    traffic = traffic_for(w)
     result = {
         "metric": "ring_attention TFLOP/s at 1 GPU (counted 4*d*Hq*allowed pairs) and % of bf16 MFMA peak",
-        "value": round(tflops, 2),
+        "value": entry["TFLOP/s"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "clock_settle": {"calls": entry["clock_settle_calls"], "seconds": args.settle_seconds,
+                         "note": "untimed calls before the warm-up, outside the timed region"},
+        "ms_per_step": entry["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {
-            "workload": w.name,
-            "batch": w.batch,
-            "q_heads": w.q_heads,
-            "kv_heads": w.kv_heads,
-            "head_dim": w.head_dim,
-            "local_queries": w.lq,
-            "keys": w.lk,
-            "kv_chunks": len(w.chunks),
-            "causal": w.causal,
-            "pos_stride": w.pos_stride,
-            "counted_flops": flops,
-        },
+        "config": dict(describe(w), counted_flops=flops),
         "roofline": {
             "bound": "mfma",
             "kernel": dominant_kernel(w),
-            "kernel_ms": round(kernel_ms, 4),
-            "achieved": round(kernel_tflops, 2),
+            "kernel_ms": entry["kernel_ms"],
+            "achieved": entry["kernel_TFLOP/s"],
             "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(kernel_tflops / peak, 4),
-            "traffic": traffic,
+            "frac": entry["frac"],
+            "traffic": traffic_for(w),
         },
-        "pct_of_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+        "pct_of_bf16_peak": round(100 * entry["TFLOP/s"] / BF16_PEAK_TFLOPS, 2),
         "kernel_source_sha256_16": source_digest(),
     }
 
+    legs = {}
     if not args.no_legs:
-        legs = {}
-        # standalone attention_chunk_stats on one shard of the share
-        k0, v0 = kc[0], vc[0]
-        ms_s = timed(lambda: ra.attention_chunk_stats(q, k0, v0, scale=w.softmax_scale), args.steps,
-                     args.warmup, torch)
-        f_s = 4 * w.head_dim * w.q_heads * w.batch * w.lq * k0.shape[2]
-        legs["attention_chunk_stats"] = {"ms": round(ms_s, 4), "TFLOP/s": round(f_s / (ms_s * 1e-3) / 1e12, 2),
-                                         "shape": f"{w.lq} queries x {k0.shape[2]} keys, {w.q_heads} heads"}
-        # standalone merge at the 32-head, d=128, 8192-row shape; 4 rotating buffer sets
-        rows, d = 32 * 8192, 128
-        sets = [(torch.randn(rows, d, device=dev), torch.rand(rows, device=dev) + 0.5,
-                 torch.randn(rows, device=dev)) for _ in range(8)]
-        it = [0]
-
-        def merge_step():
-            i = it[0]
-            it[0] = (i + 2) % 8
-            ra.merge_chunk_stats(sets[i], sets[i + 1], inplace=True)
-
-        ms_m = timed(merge_step, max(args.steps, 20), args.warmup, torch)
-        mbytes = 12 * (d + 2) * rows
-        src = torch.empty(mbytes // 8, dtype=torch.float32, device=dev)  # read + write = mbytes
-        dst = torch.empty_like(src)
-        srcs = [torch.empty_like(src) for _ in range(3)]
-        ci = [0]
-
-        def copy_step():
-            j = ci[0]
-            ci[0] = (j + 1) % 3
-            dst.copy_(srcs[j])
-
-        ms_c = timed(copy_step, max(args.steps, 20), args.warmup, torch)
-        legs["merge_chunk_stats"] = {
-            "ms": round(ms_m, 4),
-            "GB/s": round(mbytes / (ms_m * 1e-3) / 1e9, 1),
-            "bytes_per_call": mbytes,
-            "frac_of_hbm_peak": round(mbytes / (ms_m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "device_copy_GB/s": round(mbytes / (ms_c * 1e-3) / 1e9, 1),
-            "shape": f"{rows} rows x d={d}, fp32, 4 rotating buffer sets",
-        }
-        del sets, src, dst, srcs
+        legs["attention_chunk_stats_d128"] = stats_leg(q, kc[0], vc[0], w.softmax_scale, args, torch, ra)
         if w.dtype == "bf16" and w.head_dim % 8 == 0:
             legs["ring_attention_backward"] = backward_leg(w, q, kc, vc, offs, args, torch, ra)
-        result["legs"] = legs
-
+    baseline = None
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, q, kc, vc, offs, args.cpu_seconds)
+        baseline = cpu_baseline(w, q, kc, vc, offs, args.cpu_seconds)
+    del q, kc, vc
+    torch.cuda.empty_cache()
+
+    configs = {}
+    for tok in [t for t in args.configs.split(",") if t.strip()]:
+        i = int(tok)
+        if i == args.config:
+            continue
+        wi = wl.config(i)
+        e, inputs = measure_share(wi, None, 3, 0.5, torch, ra, wl, dev)
+        e["config"] = describe(wi)
+        configs[wi.name] = e
+        if i == 1 and not args.no_legs:
+            qi, kci, vci, _ = inputs
+            legs["attention_chunk_stats"] = stats_leg(qi, kci[0], vci[0], wi.softmax_scale, args, torch, ra)
+        del inputs
+        torch.cuda.empty_cache()
+    if configs:
+        result["configs"] = configs
+    if not args.no_legs:
+        legs["merge_chunk_stats"] = merge_leg(args, torch, ra, dev)
+        result["legs"] = legs
+    if baseline is not None:
+        result["cpu_baseline"] = baseline
     print(json.dumps(result), flush=True)
 
 

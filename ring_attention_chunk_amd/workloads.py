@@ -312,19 +312,51 @@ def counted_flops(w: Workload) -> int:
     return 4 * w.head_dim * w.q_heads * w.batch * unmasked_pairs_per_head(w)
 
 
-def sample_rows(w: Workload, count: int, seed: int = 0, tile: int = 128) -> List[Tuple[int, int, int]]:
-    """Stratified ``(b, h, row)`` sample: segment ends, tile edges, then seeded random rows."""
+def sample_rows(w: Workload, count: int, seed: int = 0, wg_rows: int = 256, tile: int = 64
+                ) -> List[Tuple[int, int, int]]:
+    """Stratified ``(b, h, row)`` sample of at least ``count`` rows (fewer only if the share has fewer).
+
+    Strata, each row with a seeded random batch entry and head:
+      * the first and last row of every query segment;
+      * the rows on both sides of every wave (32 rows), half-workgroup (128) and workgroup (256) edge of
+        the first and last workgroup, and of every workgroup edge in between;
+      * every row of the first and of the last workgroup of query rows;
+      * causal shares: the diagonal band, rows whose global position is within 2 of a multiple of ``tile``
+        (the mask boundary then falls at the edge of a key tile);
+      * seeded random rows up to ``count``.
+    Duplicates are dropped, so every pair appears once.
+    """
     g = np.random.default_rng([seed, 991])
-    picks = []
+    lq = w.lq
+    special = []
     starts = np.cumsum([0] + [n for _, n in w.q_segments])
-    special = set()
     for s0, s1 in zip(starts[:-1], starts[1:]):
         if s1 > s0:
-            special.update([int(s0), int(s1) - 1])
-    for t in range(tile, w.lq, tile * 7):
-        special.update([t - 1, t])
-    for i, r in enumerate(sorted(special)):
-        picks.append((i % w.batch, (i * 5) % w.q_heads, r))
-    while len(picks) < count:
-        picks.append((int(g.integers(w.batch)), int(g.integers(w.q_heads)), int(g.integers(w.lq))))
-    return picks[:max(count, 0)] if count < len(picks) else picks
+            special += [int(s0), int(s1) - 1]
+    for base in sorted({0, max(0, (lq - 1) // wg_rows * wg_rows)}):
+        for e in (32, 64, 96, 128, 160, 192, 224, 256):
+            special += [base + e - 1, base + e]
+    for t in range(wg_rows, lq, wg_rows):
+        special += [t - 1, t]
+    last_wg = max(0, (lq - 1) // wg_rows * wg_rows)
+    special += list(range(0, min(wg_rows, lq))) + list(range(last_wg, lq))
+    if w.causal:
+        qpos = q_positions(w)
+        band = np.nonzero(np.isin(qpos % tile, [0, 1, tile - 2, tile - 1]))[0]
+        special += [int(x) for x in band]
+    seen = set()
+    picks = []
+
+    def add(r):
+        key = (int(g.integers(w.batch)), int(g.integers(w.q_heads)), int(r))
+        if 0 <= r < lq and key not in seen:
+            seen.add(key)
+            picks.append(key)
+
+    for r in special:
+        add(r)
+    tries = 0
+    while len(picks) < count and tries < 50 * count:
+        add(int(g.integers(lq)))
+        tries += 1
+    return picks

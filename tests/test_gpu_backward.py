@@ -130,7 +130,44 @@ def test_backward_errors_raise():
         ra.ring_attention_backward(qf, [qf], [qf], qf, lse, qf)
 
 
-@pytest.mark.parametrize("i", [1, 2])
+def _backward_oracle_parallel(q, kc, vc, dout, qpos, offs, causal, parts):
+    """oracle.attention_backward on groups of query rows in a thread pool (one BLAS thread each): dq of each
+    row comes from its own group; dk and dv are the sums of the groups' contributions (the gradient of a
+    key is the sum over the query rows that see it). ``parts`` is a list of (head, row start, row stop)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    qn = q.float().cpu().double().numpy()
+    dn = dout.float().cpu().double().numpy()
+    kn = [c.float().cpu().double().numpy() for c in kc]
+    vn = [c.float().cpu().double().numpy() for c in vc]
+    B, Hq, Lq, d = qn.shape
+    Hkv = kn[0].shape[1]
+    group = Hq // Hkv
+
+    def run(part):
+        h, r0, r1 = part
+        hk = h // group
+        return oracle.attention_backward(qn[:, h:h + 1, r0:r1], [c[:, hk:hk + 1] for c in kn],
+                                         [c[:, hk:hk + 1] for c in vn], dn[:, h:h + 1, r0:r1],
+                                         None if qpos is None else qpos[r0:r1], offs, causal=causal)
+
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(min(len(parts), 16)) as ex:
+        res = list(ex.map(run, parts))
+    n = sum(c.shape[2] for c in kn)
+    dq = np.zeros((B, Hq, Lq, d))
+    dk = np.zeros((B, Hkv, n, d))
+    dv = np.zeros((B, Hkv, n, d))
+    for (h, r0, r1), r in zip(parts, res):
+        dq[:, h, r0:r1] = r["dq"][:, 0]
+        dk[:, h // group] += r["dk"][:, 0]
+        dv[:, h // group] += r["dv"][:, 0]
+    return dq, dk, dv
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("i", [1, 2, 3])
 def test_backward_full_size(i):
     """A full-size share in the benchmark's launch configuration: head 0 in full against the oracle,
     and on every head the sums that hold at any size: the key gradients of a head sum to zero (each row
@@ -152,11 +189,58 @@ def test_backward_full_size(i):
     sum_do = do_seen.sum(dim=(2, 3))
     assert ((dv.sum(2) - sum_do).abs() <= 1e-2 * do_seen.abs().sum(dim=(2, 3))).all()
     assert (dk.sum(2).abs() <= 1e-2 * dk.abs().sum(2)).all()
-    ref = oracle.attention_backward(q[:, :1].cpu(), [c[:, :1].cpu() for c in kc], [c[:, :1].cpu() for c in vc],
-                                    dout[:, :1].cpu(), wl.q_positions(w), w.kv_offsets, causal=w.causal)
-    _compare("dq head 0", _np(dq[:, :1]), ref["dq"])
-    _compare("dk head 0", _np(dk[:, :1]), ref["dk"])
-    _compare("dv head 0", _np(dv[:, :1]), ref["dv"])
+    assert w.q_heads == w.kv_heads  # head 0's key gradients come from query head 0 alone
+    step = 512
+    parts = [(0, r0, min(w.lq, r0 + step)) for r0 in range(0, w.lq, step)]
+    rdq, rdk, rdv = _backward_oracle_parallel(q[:, :1], [c[:, :1] for c in kc], [c[:, :1] for c in vc],
+                                              dout[:, :1], wl.q_positions(w) if w.causal else None, w.kv_offsets,
+                                              w.causal, parts)
+    _compare("dq head 0", _np(dq[:, :1]), rdq)
+    _compare("dk head 0", _np(dk[:, :1]), rdk)
+    _compare("dv head 0", _np(dv[:, :1]), rdv)
+
+
+@pytest.mark.timeout(900)
+def test_backward_long_gqa_full_share_sampled_dq():
+    """The long GQA share (8 query heads on one key/value head, 1,048,576 keys) at full size: on every head
+    the sums that hold at any size, and dq of 16 stratified rows per head against the oracle (a row's dq
+    depends on that row and every key only, so the oracle of those rows alone gives it exactly)."""
+    w = wl.config(4)
+    _say(f"backward full size {w.name}: sums and sampled dq")
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    g = torch.Generator(device=DEV).manual_seed(7)
+    dout = torch.randn(q.shape, device=DEV, generator=g).to(torch.bfloat16)
+    out, lse = ra.ring_attention(q, kc, vc, return_lse=True)
+    dq, dks, dvs = ra.ring_attention_backward(q, kc, vc, out, lse, dout)
+    torch.cuda.synchronize()
+    dk, dv = torch.cat(dks, 2), torch.cat(dvs, 2)
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    sum_do = dout.float().sum(dim=(1, 2))  # [B, d]: every row sees every key
+    assert ((dv.sum(2)[:, 0] - sum_do).abs() <= 1e-2 * dout.float().abs().sum(dim=(1, 2))).all()
+    assert (dk.sum(2).abs() <= 1e-2 * dk.abs().sum(2)).all()
+    rows = [0, 31, 32, 255, 256, 8191, 8192, 16383] + [int(x) for x in np.random.default_rng(44).choice(
+        np.arange(1, 16383), 8, replace=False)]
+    sel = torch.tensor(rows, device=DEV)
+    parts = [(h, 0, len(rows)) for h in range(w.q_heads)]
+    rdq, _, _ = _backward_oracle_parallel(q[:, :, sel], kc, vc, dout[:, :, sel], None, w.kv_offsets, False, parts)
+    _compare("dq sampled rows", _np(dq[:, :, sel]), rdq)
+
+
+@pytest.mark.timeout(900)
+def test_backward_long_gqa_keys_in_full():
+    """The long GQA share at its full key length (1,048,576 keys in 64 shards, the same key and value data)
+    with the first 128 queries of each of the 8 query heads: every key's gradient sums the contributions of
+    all 8 heads sharing its key/value head; dq, dk and dv are compared in full."""
+    base = wl.config(4)
+    w = wl.custom("long_gqa_q128_k1m", "bf16", 1, 8, 1, 128, [(0, 128)], base.chunks, False, seq_len=base.seq_len,
+                  q_std=base.q_std, seed=base.seed)
+    _say(f"backward {w.name}")
+    q, kc, vc, dout, out, lse, dq, dks, dvs = _run_case(w)
+    parts = [(h, 0, w.lq) for h in range(w.q_heads)]
+    rdq, rdk, rdv = _backward_oracle_parallel(q, kc, vc, dout, None, w.kv_offsets, False, parts)
+    _compare("dq", _np(dq), rdq)
+    _compare("dk", np.concatenate([_np(t) for t in dks], axis=2), rdk)
+    _compare("dv", np.concatenate([_np(t) for t in dvs], axis=2), rdv)
 
 
 def test_backward_very_negative_scores_with_ragged_last_tile():

@@ -8,6 +8,7 @@ checked on every case, the backward pass on every bf16 case whose head_dim
 is a multiple of 8. Tolerances are those of the other parity tests.
 """
 
+import math
 import zlib
 
 import numpy as np
@@ -89,7 +90,8 @@ def test_random_share(seed):
     _check(out.cpu().double().numpy(), ref["out"], w.dtype)
     fin = np.isfinite(ref["lse"])
     assert np.array_equal(np.isfinite(lse.cpu().numpy()), fin)
-    tol = 1e-5 if w.dtype == "f32" else 1e-2
+    # bf16: 2^-9 from rounding the summed probabilities to bf16, 2^-24 per key tile of fp32 running sum
+    tol = 1e-5 if w.dtype == "f32" else 2.0 ** -9 + math.ceil(max(w.lk, 1) / 64) * 2.0 ** -24 + 1e-5
     assert np.abs(lse.cpu().double().numpy()[fin] - ref["lse"][fin]).max(initial=0.0) <= tol
     if w.dtype != "bf16" or w.head_dim % 8 != 0 or w.lk == 0:
         return

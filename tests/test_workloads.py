@@ -90,13 +90,19 @@ def test_q_scale_of_long_gqa():
     assert w.q_std == 4.0 and w.q_heads == 8 and w.kv_heads == 1
 
 
-def test_sample_rows_cover_segment_ends():
+def test_sample_rows_cover_the_strata():
     w = wl.config(3)
-    rows = wl.sample_rows(w, 300)
+    rows = wl.sample_rows(w, 2048)
     r = {x[2] for x in rows}
-    assert {0, 4095, 4096, 8191} <= r
-    assert len(rows) == 300
+    assert {0, 4095, 4096, 8191} <= r  # segment ends
+    assert {31, 32, 127, 128, 255, 256, 8191 - 256, 8192 - 256} <= r  # wave and workgroup edges
+    assert set(range(256)) <= r and set(range(8192 - 256, 8192)) <= r  # first and last workgroup
+    qpos = wl.q_positions(w)
+    band = {i for i in range(w.lq) if qpos[i] % 64 in (0, 1, 62, 63)}
+    assert band <= r  # the diagonal band of the causal share
+    assert len(rows) >= 2048 and len(set(rows)) == len(rows)
     assert all(0 <= b < w.batch and 0 <= h < w.q_heads and 0 <= i < w.lq for b, h, i in rows)
+    assert len({h for _, h, _ in rows}) == w.q_heads  # every head appears
 
 
 def test_striped_share_bookkeeping():
