@@ -99,6 +99,7 @@ struct QSegDev {
   int64_t pos0;
   int64_t ps;  // position step between consecutive rows
 };
+static_assert(sizeof(ChunkDev) % 4 == 0 && sizeof(QSegDev) % 4 == 0, "tables are uploaded in 4-byte words");
 
 struct Params {
   const void* q;
@@ -1816,26 +1817,43 @@ namespace ra_host {
 
 // Descriptor tables travel to the device as kernel arguments: 2 KB per launch,
 // well inside the kernel argument space.
-constexpr int kUploadWords = 512;
-struct UploadArgs {
-  uint32_t w[kUploadWords];
-};
-
-__global__ __launch_bounds__(256) void upload_kernel(uint32_t* __restrict__ dst, int n, UploadArgs a) {
+__global__ __launch_bounds__(256) void upload_kernel(uint32_t* __restrict__ dst, int n, UploadWindow a) {
   for (int i = threadIdx.x; i < n; i += 256) dst[i] = a.w[i];
 }
 
-hipError_t upload_table(void* dst, const void* src, size_t bytes, hipStream_t s) {
-  const size_t words = bytes / 4;
-  for (size_t w0 = 0; w0 < words; w0 += kUploadWords) {
-    const int n = (int)(words - w0 < (size_t)kUploadWords ? words - w0 : (size_t)kUploadWords);
-    UploadArgs a;
-    memcpy(a.w, (const uint32_t*)src + w0, (size_t)n * 4);
-    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, (uint32_t*)dst + w0, n, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+void TableUpload::flush() {
+  if (fill_ == 0) return;
+  hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s_, (uint32_t*)(dst_ + base_), (int)(fill_ / 4), win_);
+  const hipError_t e = hipGetLastError();
+  if (err_ == hipSuccess) err_ = e;
+  base_ += fill_;
+  fill_ = 0;
+}
+
+void TableUpload::put(const void* p, size_t n) {
+  const char* src = (const char*)p;
+  while (n > 0) {
+    const size_t room = sizeof(win_) - fill_;
+    const size_t k = n < room ? n : room;
+    memcpy((char*)win_.w + fill_, src, k);
+    fill_ += k;
+    src += k;
+    n -= k;
+    if (fill_ == sizeof(win_)) flush();
   }
-  return hipSuccess;
+}
+
+void TableUpload::zero_to(size_t total) {
+  static const uint32_t zeros[64] = {};
+  while (size() < total) {
+    const size_t k = total - size() < sizeof(zeros) ? total - size() : sizeof(zeros);
+    put(zeros, k);
+  }
+}
+
+hipError_t TableUpload::finish() {
+  flush();
+  return err_;
 }
 
 constexpr int kTimerSlots = 512;
@@ -2046,17 +2064,16 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0)
     return fail(RA_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, workspace_bytes);
 
-  // Descriptor tables: chunks (non-empty ones only; order kept) then query segments.
-  char* host = (char*)calloc(1, tbytes > 0 ? tbytes : 1);
-  if (!host) return fail(RA_ERR_UNSUPPORTED, "host allocation failed");
+  // Descriptor tables, written straight into the workspace on `stream`: the
+  // non-empty chunks in list order, then the query segments.
   const size_t cbytes = align256(sizeof(ChunkDev) * (size_t)n_chunks);
-  ChunkDev* hc = (ChunkDev*)host;
-  QSegDev* hqs = (QSegDev*)(host + cbytes);
+  hipStream_t hs = (hipStream_t)stream;
+  TableUpload up(workspace, hs);
   int nc = 0;
   int64_t start = 0;
   for (int c = 0; c < n_chunks; ++c) {
     if (chunks[c].len == 0) continue;
-    ChunkDev& d = hc[nc++];
+    ChunkDev d = {};
     d.k = chunks[c].k;
     d.v = chunks[c].v;
     d.start = start;
@@ -2066,19 +2083,23 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
     d.ss = chunks[c].stride_s;
     d.pos0 = (int32_t)chunks[c].global_offset;
     d.ps = (int32_t)pos_step(chunks[c].pos_stride);
+    up.put(&d, sizeof(d));
+    ++nc;
     start += chunks[c].len;
   }
+  up.zero_to(cbytes);
   int64_t row0 = 0;
   for (int s = 0; s < n_q_segments; ++s) {
-    hqs[s].row0 = row0;
-    hqs[s].len = q_segments[s].len;
-    hqs[s].pos0 = q_segments[s].global_offset;
-    hqs[s].ps = pos_step(q_segments[s].pos_stride);
+    QSegDev g = {};
+    g.row0 = row0;
+    g.len = q_segments[s].len;
+    g.pos0 = q_segments[s].global_offset;
+    g.ps = pos_step(q_segments[s].pos_stride);
+    up.put(&g, sizeof(g));
     row0 += q_segments[s].len;
   }
-  hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = upload_table(workspace, host, tbytes, hs);
-  free(host);
+  up.zero_to(tbytes);
+  hipError_t e = up.finish();
   if (e != hipSuccess) return hip_fail(e, "ring_attention descriptor upload");
 
   Params p = {};

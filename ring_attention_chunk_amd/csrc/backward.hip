@@ -570,6 +570,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(int64_t n4, int ns, cons
 struct BwdSeg {
   int64_t row0, len, pos0, ps;
 };
+static_assert(sizeof(BwdChunk) % 4 == 0 && sizeof(BwdSeg) % 4 == 0, "tables are uploaded in 4-byte words");
 
 __global__ __launch_bounds__(256) void bwd_positions_kernel(const BwdChunk* __restrict__ chunks, int n_chunks,
                                                             const BwdSeg* __restrict__ segs, int n_segs,
@@ -740,19 +741,16 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
                 workspace_bytes);
 
   // Chunk and query-segment descriptors go to the workspace as kernel arguments
-  // (host memory is read only during this call); the position tables are then
+  // (host arrays are read only during this call); the position tables are then
   // built from them on the device.
-  const size_t dbytes = L.qpos;  // chunk table, then segment table
-  char* host = (char*)calloc(1, dbytes);
-  if (!host) return fail(RA_ERR_UNSUPPORTED, "host allocation failed");
-  BwdChunk* hc = (BwdChunk*)(host + L.chunks);
-  BwdSeg* hs_ = (BwdSeg*)(host + L.segs);
+  hipStream_t hs = (hipStream_t)stream;
+  TableUpload up(workspace, hs);
   int nc = 0;
   int64_t start = 0;
   for (int c = 0; c < n_chunks; ++c) {
     const ra_kv_chunk& ch = chunks[c];
     if (ch.len == 0) continue;
-    BwdChunk& d = hc[nc++];
+    BwdChunk d = {};
     d.k = ch.k;
     d.v = ch.v;
     d.start = start;
@@ -762,19 +760,23 @@ int ra_ring_attention_backward(int dtype, int batch, int q_heads, int kv_heads, 
     d.ss = ch.stride_s;
     d.pos0 = (int32_t)ch.global_offset;
     d.ps = (int32_t)pos_step(ch.pos_stride);
+    up.put(&d, sizeof(d));
+    ++nc;
     start += ch.len;
   }
+  up.zero_to(L.segs);
   int64_t row0 = 0;
   for (int s = 0; s < n_q_segments; ++s) {
-    hs_[s].row0 = row0;
-    hs_[s].len = q_segments[s].len;
-    hs_[s].pos0 = q_segments[s].global_offset;
-    hs_[s].ps = pos_step(q_segments[s].pos_stride);
+    BwdSeg g = {};
+    g.row0 = row0;
+    g.len = q_segments[s].len;
+    g.pos0 = q_segments[s].global_offset;
+    g.ps = pos_step(q_segments[s].pos_stride);
+    up.put(&g, sizeof(g));
     row0 += q_segments[s].len;
   }
-  hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = upload_table(workspace, host, dbytes, hs);
-  free(host);
+  up.zero_to(L.qpos);
+  hipError_t e = up.finish();
   if (e != hipSuccess) return hip_fail(e, "ring_attention_backward descriptor upload");
   {
     char* ws = (char*)workspace;

@@ -36,12 +36,36 @@ bool chunk_vec_ok(const ra_kv_chunk& c, int head_dim, int64_t elem);
 void timer_begin(hipStream_t s);
 void timer_end(hipStream_t s);
 
-// Stream-ordered copy of `bytes` (a multiple of 4) of host memory to device
-// memory at `dst`, carried as kernel arguments of small copy kernels: the
-// runtime captures arguments when a launch is enqueued, so the host bytes need
-// to stay valid only for this call, and no host-to-device copy engine or
-// staging buffer is involved. Meant for descriptor tables of a few KB.
-hipError_t upload_table(void* dst, const void* src, size_t bytes, hipStream_t s);
+// Stream-ordered writer of a descriptor table into device memory at `dst`.
+// Appended bytes gather in a fixed 2 KB window that reaches the device as the
+// kernel arguments of a small copy kernel; the runtime captures arguments when
+// a launch is enqueued, so the caller's host arrays are read only during the
+// call, and neither host nor device memory is allocated. Every append and
+// padding is a whole number of 4-byte words.
+constexpr int kUploadWords = 512;
+struct UploadWindow {
+  uint32_t w[kUploadWords];
+};
+
+class TableUpload {
+ public:
+  TableUpload(void* dst, hipStream_t s) : dst_((char*)dst), s_(s) {}
+  void put(const void* p, size_t n);
+  // zero bytes until the table is `total` bytes long
+  void zero_to(size_t total);
+  size_t size() const { return base_ + fill_; }
+  // uploads the last window; returns the first launch error, if any
+  hipError_t finish();
+
+ private:
+  void flush();
+  char* dst_;
+  hipStream_t s_;
+  size_t base_ = 0;  // bytes already sent
+  size_t fill_ = 0;  // bytes in the window
+  hipError_t err_ = hipSuccess;
+  UploadWindow win_;
+};
 
 }  // namespace ra_host
 
