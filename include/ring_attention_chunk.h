@@ -166,6 +166,33 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
                       void* workspace, size_t workspace_bytes, float* out, float* lse,
                       void* stream);
 
+/* Size, in bytes, of the device array that ra_ring_attention_noalloc uses as
+ * its workspace (one per GPU, held until the process ends). */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* ra_ring_attention for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP stream capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments, meaning and results as
+ * ra_ring_attention (bit-identical output and lse), without the workspace:
+ * the descriptor tables and key-range partials go to a file-scope device
+ * array of RA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds
+ * until the process ends. The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine, no host allocation). The first call on a
+ * device, with that device current, looks up the array's address there
+ * (hipGetSymbolAddress); make that first call outside stream capture.
+ * Returns RA_ERR_WORKSPACE, before any HIP call, when the tables and
+ * key-range partials of the call exceed RA_NOALLOC_SCRATCH_BYTES (they never
+ * exceed ra_ring_workspace_bytes(...) for the call).
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; each call writes every byte it reads on its own stream first, so
+ * nothing needs clearing, but calls that overlap on one GPU (on different
+ * streams, or from several host threads) race and must be serialised by the
+ * caller. The stream must belong to the current device. */
+int ra_ring_attention_noalloc(int dtype, int batch, int q_heads, int kv_heads, int head_dim,
+                              const void* q, const ra_q_segment* q_segments, int n_q_segments,
+                              const ra_kv_chunk* chunks, int n_chunks, int causal, float scale,
+                              float* out, float* lse, void* stream);
+
 /* Device workspace, in bytes, that ra_ring_attention_backward needs: the
  * chunk and query segment tables, the query and key positions (4 bytes per
  * query row and per key, built on the device), per-32-row position bounds,

@@ -29,6 +29,7 @@ EXPORTS = (
     "ra_merge_chunk_stats",
     "ra_ring_workspace_bytes",
     "ra_ring_attention",
+    "ra_ring_attention_noalloc",
     "ra_ring_backward_workspace_bytes",
     "ra_ring_attention_backward",
     "ra_kernel_timer",
@@ -85,6 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_ring_attention.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                       ctypes.POINTER(KVChunk), i32, i32, f32, vp, sz, vp, vp, vp]
     lib.ra_ring_attention.restype = i32
+    lib.ra_ring_attention_noalloc.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
+                                              ctypes.POINTER(KVChunk), i32, i32, f32, vp, vp, vp]
+    lib.ra_ring_attention_noalloc.restype = i32
     lib.ra_ring_backward_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32, i32]
     lib.ra_ring_backward_workspace_bytes.restype = sz
     lib.ra_ring_attention_backward.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
@@ -295,6 +299,37 @@ def ring_attention(query, key_chunks: Sequence, value_chunks: Sequence, q_global
                                out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(q))
     _check(lib, st, "ring_attention")
     return (out, lse) if return_lse else out
+
+
+def ring_attention_noalloc(query, key_chunks: Sequence, value_chunks: Sequence, q_global_offset: QOffset = 0,
+                           kv_global_offsets: Optional[Sequence[int]] = None, causal: bool = False,
+                           scale: Optional[float] = None, kv_position_strides: Optional[Sequence[int]] = None,
+                           out=None, lse=None):
+    """:func:`ring_attention` through ``ra_ring_attention_noalloc``: no workspace, no device allocation in the
+    library (its tables and partials live in a per-GPU static array of ``RA_NOALLOC_SCRATCH_BYTES``).
+
+    Pass ``out`` [B, Hq, Lq, d] fp32 (and optionally ``lse`` [B, Hq, Lq] fp32), contiguous, to make the whole
+    call allocation-free; without them this wrapper allocates them with torch. Returns ``out`` (and
+    ``lse`` when given). Calls that overlap on one GPU race on the shared array."""
+    torch = _torch()
+    lib = load_library()
+    Hkv, descs, n, segs, nseg = _marshal(query, key_chunks, value_chunks, q_global_offset, kv_global_offsets,
+                                         kv_position_strides)
+    if not query.is_contiguous():
+        raise RingAttentionError("the allocation-free call needs a contiguous query")
+    B, Hq, Lq, d = query.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, Lq, d), dtype=torch.float32, device=query.device)
+    for t, shape in ((out, (B, Hq, Lq, d)), (lse, (B, Hq, Lq))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise RingAttentionError(f"outputs must be contiguous fp32 tensors of shape {shape}")
+    st = lib.ra_ring_attention_noalloc(_dtype_code(query), B, Hq, Hkv, d, query.data_ptr(), segs, nseg, descs, n,
+                                       int(bool(causal)), float(scale), out.data_ptr(),
+                                       lse.data_ptr() if lse is not None else None, _stream(query))
+    _check(lib, st, "ring_attention_noalloc")
+    return (out, lse) if lse is not None else out
 
 
 def _marshal(query, key_chunks, value_chunks, q_global_offset, kv_global_offsets, kv_position_strides):

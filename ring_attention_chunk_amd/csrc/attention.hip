@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <mutex>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -2018,10 +2020,46 @@ int ra_merge_chunk_stats(int64_t rows, int head_dim, float* acc_u, float* acc_l,
   return RA_OK;
 }
 
-int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
-                      const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks, int n_chunks,
-                      int causal, float scale, void* workspace, size_t workspace_bytes, float* out, float* lse,
-                      void* stream) {
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Workspace of the allocation-free ring call: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends. Host code
+// never uses the array's name as an address: the address on each device comes
+// from hipGetSymbolAddress, looked up once per device with that device current.
+namespace {
+constexpr size_t kScratchBytes = RA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Address of `scratch` on the current device (looked up on the first call per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "ring_attention_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_ERR_UNSUPPORTED, "device index %d is beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "ring_attention_noalloc: hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr || (uintptr_t)ptr % 256 != 0)
+      return fail(RA_ERR_HIP, "ring_attention_noalloc: scratch array at an unusable address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RA_OK;
+}
+
+// The ring call. With use_scratch the workspace is the device's `scratch`
+// array (workspace and workspace_bytes are ignored).
+int ring_attention_call(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
+                        const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks, int n_chunks,
+                        int causal, float scale, void* workspace, size_t workspace_bytes, bool use_scratch,
+                        float* out, float* lse, void* stream) {
   g_err[0] = 0;
   int st = check_dims(dtype, batch, q_heads, kv_heads, head_dim);
   if (st) return st;
@@ -2060,7 +2098,17 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
   if (nblocks > 0x7fffffffLL) return fail(RA_ERR_UNSUPPORTED, "grid too large");
   const int64_t rows = (int64_t)batch * q_heads * lq;
   const size_t tbytes = table_bytes(n_chunks, n_q_segments);
-  const size_t need = ra_ring_workspace_bytes(batch, q_heads, head_dim, lq, lk, n_chunks, n_q_segments);
+  // the public size covers either kernel's key-range cut; the static scratch only needs the bytes this
+  // call uses: its tables and the partials of the cut it runs with
+  const size_t need = use_scratch ? tbytes + partial_bytes(nsplit, rows, head_dim)
+                                  : ra_ring_workspace_bytes(batch, q_heads, head_dim, lq, lk, n_chunks, n_q_segments);
+  if (use_scratch) {
+    if (need > kScratchBytes)
+      return fail(RA_ERR_WORKSPACE, "this share needs %zu bytes of workspace; the static scratch holds %zu", need,
+                  kScratchBytes);
+    if ((st = scratch_address(&workspace))) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0)
     return fail(RA_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need, workspace_bytes);
 
@@ -2135,6 +2183,25 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
     if (e != hipSuccess) return hip_fail(e, "ring_attention combine launch");
   }
   return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
+                      const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks, int n_chunks,
+                      int causal, float scale, void* workspace, size_t workspace_bytes, float* out, float* lse,
+                      void* stream) {
+  return ring_attention_call(dtype, batch, q_heads, kv_heads, head_dim, q, q_segments, n_q_segments, chunks,
+                             n_chunks, causal, scale, workspace, workspace_bytes, false, out, lse, stream);
+}
+
+int ra_ring_attention_noalloc(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
+                              const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks,
+                              int n_chunks, int causal, float scale, float* out, float* lse, void* stream) {
+  return ring_attention_call(dtype, batch, q_heads, kv_heads, head_dim, q, q_segments, n_q_segments, chunks,
+                             n_chunks, causal, scale, nullptr, 0, true, out, lse, stream);
 }
 
 }  // extern "C"

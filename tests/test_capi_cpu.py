@@ -117,6 +117,21 @@ def test_ring_validation_codes(lib):
     assert b"workspace" in lib.ra_last_error()
 
 
+def test_noalloc_refuses_a_share_beyond_its_scratch(lib):
+    """Host-side check only: a short query share against many keys needs key-range partials beyond the static
+    scratch array, and the allocation-free call refuses it before any HIP call."""
+    seg = (api.QSegment * 1)(api.QSegment(2048, 0))
+    ch = (api.KVChunk * 1)(api.KVChunk(FAKE, FAKE, 1 << 20, 0, 0, 0, 128))
+    need = lib.ra_ring_workspace_bytes(1, 8, 128, 2048, 1 << 20, 1, 1)
+    assert need > 32 << 20
+    st = lib.ra_ring_attention_noalloc(1, 1, 8, 1, 128, FAKE, seg, 1, ch, 1, 0, 0.088, FAKE, None, None)
+    assert st == 6
+    assert b"static scratch" in lib.ra_last_error()
+    # the same validation as the workspace call before that
+    assert lib.ra_ring_attention_noalloc(1, 1, 3, 2, 64, FAKE, seg, 1, ch, 1, 0, 0.1, FAKE, None, None) == 2
+    assert lib.ra_ring_attention_noalloc(1, 1, 8, 1, 128, FAKE, seg, 1, ch, 1, 0, 0.1, None, None, None) == 1
+
+
 def test_empty_work_is_a_no_op(lib):
     seg = (api.QSegment * 1)(api.QSegment(0, 0))
     assert _ring(lib, segs=seg) == 0  # no queries: nothing to launch
