@@ -19,6 +19,12 @@ Two independent statements of what the method computes live here:
   the chain rule ("Ring Attention: Distributed Reads with Online Softmax",
   section "Backward must aggregate shared dependencies"). It is pinned by
   central finite differences of :mod:`oracle.direct` and by torch autograd.
+* :mod:`oracle.block_sparse` -- ordinary attention restricted to the keys a
+  block mask over global positions allows ("Ring Attention: Distributed Reads
+  with Online Softmax", section "What is preserved, what is distributed?": the
+  method composes with sparse patterns), optionally combined with the causal
+  mask. It expands the block mask to the full boolean matrix and evaluates
+  masked softmax attention; pinned by ``tests/test_oracle_block_sparse.py``.
 * :mod:`oracle.online_softmax` -- the exercise's three functions written out
   in fp64 (chunk statistics, the rescale-to-shared-max merge, and the fold
   over chunks followed by one normalisation). It is the reference for the
@@ -35,12 +41,15 @@ shares, with planted bookkeeping mistakes that the pin must catch
 """
 
 from .backward import attention_backward
+from .block_sparse import attention_block_sparse, expand_block_mask
 from .direct import attention, attention_rows, key_positions, query_positions
 from .online_softmax import chunk_stats, merge_chunk_stats, ring_attention_fold, normalize
 
 __all__ = [
     "attention",
     "attention_backward",
+    "attention_block_sparse",
+    "expand_block_mask",
     "attention_rows",
     "key_positions",
     "query_positions",
