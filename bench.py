@@ -248,6 +248,44 @@ def stats_leg(q, k0, v0, scale, args, torch, ra):
             "steps": steps, "shape": f"{Lq} queries x {k0.shape[2]} keys, {Hq} heads, d={d}"}
 
 
+def block_sparse_leg(torch, ra, wl, dev="cuda:0"):
+    """ring_attention_block_sparse on a non-causal share of 8 heads, d = 128, 8192 queries against 65536 keys
+    in 8 shards, under random block masks of 256 x 512 positions at several densities. Counted flops: 4 * d
+    per allowed (query, key) pair and query head, so equal TFLOP/s at every density means time proportional
+    to density."""
+    import numpy as np
+
+    P, L = 8, 8192
+    w = wl.custom("block_sparse_h8_d128_q8k_k64k", "bf16", 1, 8, 8, 128, [(0, L)],
+                  [(j * L, L) for j in wl.ring_order(0, P)], False, seed=106)
+    q, k, v, kc, vc = wl.generate_torch(w, dev)
+    bq, bk = 256, 512
+    nqb, nkb = w.seq_len // bq, w.seq_len // bk
+    rows = {}
+    base_ms = None
+    for density in (1.0, 0.5, 0.25, 0.125):
+        rng = np.random.default_rng([106, int(density * 1000)])
+        m = (rng.random((nqb, nkb)) < density) if density < 1 else np.ones((nqb, nkb), bool)
+        mask = torch.from_numpy(m.astype(np.uint8)).to(dev)
+        qpos = np.arange(w.lq)
+        allowed = int(m[qpos // bq].sum()) * bk  # every key block holds bk keys
+        flops = 4 * w.head_dim * w.q_heads * w.batch * allowed
+        ws = torch.empty(ra.api.load_library().ra_block_sparse_workspace_bytes(
+            1, w.q_heads, w.head_dim, w.lq, w.lk, len(kc), 1, nqb, nkb), dtype=torch.uint8, device=dev)
+
+        def step():
+            return ra.ring_attention_block_sparse(q, kc, vc, mask, bq, bk, 0, w.kv_offsets, workspace=ws)
+
+        ms, kernel_ms = timed_with_kernel(step, 20, 3, torch, ra.api)
+        base_ms = base_ms or ms
+        rows[f"{density:g}"] = {"block_density": round(float(m.mean()), 4), "ms": round(ms, 4),
+                                "kernel_ms": round(kernel_ms, 4),
+                                "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2),
+                                "kernel_TFLOP/s": round(flops / (kernel_ms * 1e-3) / 1e12, 2),
+                                "ms_over_dense_ms": round(ms / base_ms, 4)}
+    return {"shape": f"{w.name}: {bq} x {bk} position blocks, random masks", "by_density": rows}
+
+
 def merge_leg(args, torch, ra, dev="cuda:0"):
     """Standalone merge at the 32-head, d=128, 8192-row shape with 4 rotating buffer pairs (1.6 GB, beyond
     the 256 MB last-level cache), next to a device copy of the same byte count."""
@@ -716,6 +754,7 @@ def main():
         result["configs"] = configs
     if not args.no_legs:
         legs["merge_chunk_stats"] = merge_leg(args, torch, ra, dev)
+        legs["ring_attention_block_sparse"] = block_sparse_leg(torch, ra, wl, dev)
         result["legs"] = legs
     if baseline is not None:
         result["cpu_baseline"] = baseline

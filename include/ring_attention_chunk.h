@@ -193,6 +193,43 @@ int ra_ring_attention_noalloc(int dtype, int batch, int q_heads, int kv_heads, i
                               const ra_kv_chunk* chunks, int n_chunks, int causal, float scale,
                               float* out, float* lse, void* stream);
 
+/* Device workspace, in bytes, that ra_ring_attention_block_sparse needs for
+ * this shape and a block mask of n_qblocks x n_kblocks: that of
+ * ra_ring_attention, plus the mask packed one bit per block and, per query
+ * tile, the list of key tiles to visit. A multiple of 256. */
+size_t ra_block_sparse_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys,
+                                       int n_chunks, int n_q_segments, int64_t n_qblocks, int64_t n_kblocks);
+
+/* ring_attention under a block-sparse mask.
+ * "Ring Attention: Distributed Reads with Online Softmax", section "What is
+ * preserved, what is distributed?": the method composes with tiled kernels
+ * and sparse patterns. The pages give no pattern; here it is a block mask over
+ * GLOBAL positions (like the causal mask, section "Causal masks depend on
+ * global positions"), so it means the same on every device and for every
+ * split of the keys into chunks: positions fall into query blocks of block_q
+ * and key blocks of block_k positions, and a key at position k is allowed for
+ * a query at position p when block_mask[p / block_q][k / block_k] != 0 and,
+ * with causal != 0, k <= p. The result is ordinary attention restricted to the
+ * allowed keys; rows with none give out = 0 and lse = -inf.
+ *  block_mask  DEVICE pointer, row-major bytes [n_qblocks][n_kblocks] (any
+ *              nonzero byte allows the block pair), read on `stream` during
+ *              the call; every query and key position must lie below
+ *              n_qblocks * block_q and n_kblocks * block_k.
+ *  block_q, block_k  powers of two, 1 .. 2^30.
+ *  workspace   >= ra_block_sparse_workspace_bytes(...) bytes, 256-byte
+ *              aligned: the descriptor tables, the packed mask and the key
+ *              tiles each query tile visits are built there on `stream`.
+ * Other arguments as for ra_ring_attention. Key tiles with no allowed pair for
+ * any query of a workgroup are not visited; visited tiles are masked per key.
+ * For a fixed ordered key sequence the output is bit-identical for every split
+ * of it into chunks, and with an all-ones mask it is ra_ring_attention's. */
+int ra_ring_attention_block_sparse(int dtype, int batch, int q_heads, int kv_heads, int head_dim,
+                                   const void* q, const ra_q_segment* q_segments, int n_q_segments,
+                                   const ra_kv_chunk* chunks, int n_chunks, int causal, float scale,
+                                   const uint8_t* block_mask, int64_t n_qblocks, int64_t n_kblocks,
+                                   int64_t block_q, int64_t block_k, void* workspace, size_t workspace_bytes,
+                                   float* out, float* lse, void* stream);
+
 /* Device workspace, in bytes, that ra_ring_attention_backward needs: the
  * chunk and query segment tables, the query and key positions (4 bytes per
  * query row and per key, built on the device), per-32-row position bounds,

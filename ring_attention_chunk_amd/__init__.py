@@ -14,6 +14,7 @@ from .api import (
     merge_chunk_stats,
     ring_attention,
     ring_attention_backward,
+    ring_attention_block_sparse,
 )
 
 __all__ = [
@@ -24,4 +25,5 @@ __all__ = [
     "merge_chunk_stats",
     "ring_attention",
     "ring_attention_backward",
+    "ring_attention_block_sparse",
 ]

@@ -30,6 +30,8 @@ EXPORTS = (
     "ra_ring_workspace_bytes",
     "ra_ring_attention",
     "ra_ring_attention_noalloc",
+    "ra_block_sparse_workspace_bytes",
+    "ra_ring_attention_block_sparse",
     "ra_ring_backward_workspace_bytes",
     "ra_ring_attention_backward",
     "ra_kernel_timer",
@@ -89,6 +91,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_ring_attention_noalloc.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
                                               ctypes.POINTER(KVChunk), i32, i32, f32, vp, vp, vp]
     lib.ra_ring_attention_noalloc.restype = i32
+    lib.ra_block_sparse_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32, i32, i64, i64]
+    lib.ra_block_sparse_workspace_bytes.restype = sz
+    lib.ra_ring_attention_block_sparse.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
+                                                   ctypes.POINTER(KVChunk), i32, i32, f32, vp, i64, i64, i64, i64, vp,
+                                                   sz, vp, vp, vp]
+    lib.ra_ring_attention_block_sparse.restype = i32
     lib.ra_ring_backward_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32, i32]
     lib.ra_ring_backward_workspace_bytes.restype = sz
     lib.ra_ring_attention_backward.argtypes = [i32, i32, i32, i32, i32, vp, ctypes.POINTER(QSegment), i32,
@@ -330,6 +338,46 @@ def ring_attention_noalloc(query, key_chunks: Sequence, value_chunks: Sequence, 
                                        lse.data_ptr() if lse is not None else None, _stream(query))
     _check(lib, st, "ring_attention_noalloc")
     return (out, lse) if lse is not None else out
+
+
+def ring_attention_block_sparse(query, key_chunks: Sequence, value_chunks: Sequence, block_mask, block_q: int,
+                                block_k: int, q_global_offset: QOffset = 0,
+                                kv_global_offsets: Optional[Sequence[int]] = None, causal: bool = False,
+                                scale: Optional[float] = None, return_lse: bool = False, workspace=None,
+                                kv_position_strides: Optional[Sequence[int]] = None):
+    """:func:`ring_attention` restricted by a block mask over global positions.
+
+    ``block_mask`` is a [n_qblocks, n_kblocks] bool or uint8 tensor on the GPU: a query at position p may see a
+    key at position k when ``block_mask[p // block_q, k // block_k]`` (and, with ``causal``, k <= p). Block
+    sizes are powers of two. Other arguments as for :func:`ring_attention`.
+    """
+    torch = _torch()
+    lib = load_library()
+    Hkv, descs, n, segs, nseg = _marshal(query, key_chunks, value_chunks, q_global_offset, kv_global_offsets,
+                                         kv_position_strides)
+    _require_gpu(block_mask)
+    if block_mask.dim() != 2 or block_mask.dtype not in (torch.bool, torch.uint8):
+        raise RingAttentionError("block_mask must be a 2-D bool or uint8 tensor")
+    m = block_mask.to(torch.uint8).contiguous()
+    q = query.contiguous()
+    B, Hq, Lq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    total_keys = sum(int(k.shape[2]) for k in key_chunks)
+    need = lib.ra_block_sparse_workspace_bytes(B, Hq, d, Lq, total_keys, n, nseg, int(m.shape[0]), int(m.shape[1]))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() < need or workspace.data_ptr() % 256 != 0:
+        raise RingAttentionError(f"workspace must hold {need} bytes at a 256-byte aligned address")
+    out = torch.empty((B, Hq, Lq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.ra_ring_attention_block_sparse(_dtype_code(q), B, Hq, Hkv, d, q.data_ptr(), segs, nseg, descs, n,
+                                            int(bool(causal)), float(scale), m.data_ptr(), int(m.shape[0]),
+                                            int(m.shape[1]), int(block_q), int(block_k), workspace.data_ptr(),
+                                            workspace.numel(), out.data_ptr(),
+                                            lse.data_ptr() if lse is not None else None, _stream(q))
+    _check(lib, st, "ring_attention_block_sparse")
+    return (out, lse) if return_lse else out
 
 
 def _marshal(query, key_chunks, value_chunks, q_global_offset, kv_global_offsets, kv_position_strides):

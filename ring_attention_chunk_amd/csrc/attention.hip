@@ -122,6 +122,14 @@ struct Params {
   double kinv;  // 1 / kps
   float scale;  // softmax scale
   float c2;     // scale * log2(e)
+  // block-sparse calls: per query tile, the ascending list of key tiles that hold
+  // a visible pair (sp_count entries of the row of sp_cap), and the block mask
+  // packed 32 key blocks per word, sp_rw words per query block
+  const int* sp_list;
+  const int* sp_count;
+  const uint32_t* sp_bits;
+  int sp_cap, sp_rw;
+  int sp_lgq, sp_lgk;  // log2 of the query and key block sizes (positions)
 };
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
@@ -181,9 +189,10 @@ struct TileInfo {
   int cend;        // index in the concatenation one past the last key of chunk `cursor`
   const char* kp;  // address of the tile's first key row (batch and head applied)
   const char* vp;  // same for values
+  int li;          // block-sparse walk: index of the tile in the work item's list
 };
 
-template <int MODE, int ELEM, int TB = BN>
+template <int MODE, int ELEM, int TB = BN, bool SKIP = true>
 __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor, int end, int qmax, int b,
                                               int hk) {
   TileInfo ti;
@@ -211,7 +220,7 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
         ++c;
         cc = chunk_at<MODE>(p, c);
       }
-      if (kmin > qmax) {
+      if (SKIP && kmin > qmax) {
         // nothing here is visible, and positions only grow along a chunk, so
         // no later key of chunk `cursor` is visible either: go on at the tile
         // that holds the chunk's end
@@ -232,8 +241,10 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
     ti.cend = (int)(ch.start + ch.len);
     ti.kp = (const char*)ch.k + off * ELEM;
     ti.vp = (const char*)ch.v + off * ELEM;
+    ti.li = 0;
     return ti;
   }
+  ti.li = 0;
   ti.t = end;
   ti.cursor = cursor;
   ti.flags = 1;
@@ -266,6 +277,68 @@ __device__ __forceinline__ TileInfo successor(const Params& p, const TileInfo& t
     return n;
   }
   return next_tile<MODE, ELEM, TB>(p, nt, ti.cursor, end, qmax, b, hk);
+}
+
+// Reads of tables the kernels never write, through the constant address space:
+// a uniform address then becomes a scalar load, which leaves the vector memory
+// counter (that the LDS copy pipeline waits on) alone.
+typedef const __attribute__((address_space(4))) int* cint_ptr;
+typedef const __attribute__((address_space(4))) uint32_t* cu32_ptr;
+__device__ __forceinline__ int cload(const int* p) { return *(cint_ptr)p; }
+__device__ __forceinline__ uint32_t cload(const uint32_t* p) { return *(cu32_ptr)p; }
+
+// Block-sparse walk: the tiles of a work item are entries [first, end) of its
+// query tile's list (ascending tile indices). No causal skipping here: the
+// list already holds only tiles with a visible pair.
+struct SparseWalk {
+  const int* list;
+  int end;  // one past the work item's last entry
+};
+
+// Entries of `list` (n ascending tile indices) below tile t.
+__device__ __forceinline__ int lower_entry(const int* list, int n, int t) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (cload(list + mid) < t) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+template <int MODE, int ELEM, int TB = BN>
+__device__ __forceinline__ TileInfo sparse_tile(const Params& p, const SparseWalk& sw, int e, int cursor, int end,
+                                                int qmax, int b, int hk) {
+  if (e >= sw.end) {
+    TileInfo ti = next_tile<MODE, ELEM, TB, false>(p, end, cursor, end, qmax, b, hk);
+    ti.li = e;
+    return ti;
+  }
+  TileInfo ti = next_tile<MODE, ELEM, TB, false>(p, cload(sw.list + e), cursor, end, qmax, b, hk);
+  ti.li = e;
+  return ti;
+}
+
+// The entry after `ti`; a tile right after `ti` in the same chunk follows by
+// scalar arithmetic, as in the dense walk.
+template <int MODE, int ELEM, int TB = BN>
+__device__ __forceinline__ TileInfo sparse_successor(const Params& p, const SparseWalk& sw, const TileInfo& ti,
+                                                     int end, int qmax, int b, int hk) {
+  const int e = ti.li + 1;
+  if (e < sw.end) {
+    const int nt = cload(sw.list + e);
+    if (nt == ti.t + 1 && ti.flags == 1 && (int64_t)(nt + 1) * TB <= ti.cend) {
+      TileInfo n = ti;
+      n.t = nt;
+      n.li = e;
+      n.pos0 = ti.pos0 + TB * ti.ps;
+      n.kmin = ti.kmin + TB * ti.ps;
+      n.kmax = ti.kmax + TB * ti.ps;
+      n.kp = ti.kp + (int64_t)TB * ti.ss * ELEM;
+      n.vp = ti.vp + (int64_t)TB * ti.ss * ELEM;
+      return n;
+    }
+  }
+  return sparse_tile<MODE, ELEM, TB>(p, sw, e, ti.cursor, end, qmax, b, hk);
 }
 
 // Key and value row addresses and position of tile row r; false past the last key.
@@ -669,13 +742,15 @@ __device__ __forceinline__ int wave_mode(const TileInfo& ti, int wqmin, int wqma
 // Work item of a workgroup and the query row of each lane.
 struct Work {
   int b, hk, hq, split;
+  int qt;                   // query tile (rows qt * rows per workgroup onwards)
   int64_t qrow_idx;         // (batch, head, row) index of the lane's query row
   bool valid;               // the lane's row exists
   int qpos;                 // global position of the lane's query (causal), else kPosAll
+  int spos;                 // global position of the lane's query (block-sparse calls), else 0
   int wqmin, wqmax, gqmax;  // bounds of the query positions over the wave and the workgroup
 };
 
-template <int MODE, int W = kWaves>
+template <int MODE, int W = kWaves, bool SP = false>
 __device__ __forceinline__ Work decode_work(const Params& p, int* qred, int wave, int lane) {
   Work wk;
   // Blocks are dealt to the 8 XCDs round-robin; remap so that each XCD gets a
@@ -697,9 +772,11 @@ __device__ __forceinline__ Work decode_work(const Params& p, int* qred, int wave
   if (MODE == kRingCausal) qt = p.n_qt - 1 - qt;  // later queries see more keys: start them first
   wk.hq = wk.hk * group + g;
 
+  wk.qt = qt;
   const int64_t row = (int64_t)qt * (32 * W) + wave * 32 + (lane & 31);
   wk.valid = row < p.Lq;
   wk.qrow_idx = ((int64_t)wk.b * p.Hq + wk.hq) * p.Lq + (wk.valid ? row : 0);
+  wk.spos = (SP && wk.valid) ? query_pos(p, row) : 0;
 
   wk.qpos = kPosAll;
   wk.wqmin = kPosAll;
@@ -799,12 +876,15 @@ __device__ __forceinline__ TileInfo uniform(TileInfo t) {
   t.cend = __builtin_amdgcn_readfirstlane(t.cend);
   t.kp = uniform_ptr(t.kp);
   t.vp = uniform_ptr(t.vp);
+  t.li = __builtin_amdgcn_readfirstlane(t.li);
   return t;
 }
 
 // fp32 kernel: one tile per iteration, K and V of the next tile fetched from
 // HBM into registers while the current tile is computed.
-template <class T, int DP, int MODE>
+// With SP (block-sparse calls) the tiles come from the work item's list and
+// every score of a visited tile is checked against the block mask as well.
+template <class T, int DP, int MODE, bool SP = false>
 __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   using O = Ops<T, DP>;
   __shared__ __attribute__((aligned(16))) char kbuf[2][O::K_BYTES];
@@ -816,7 +896,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   const int wave = tid >> 6;
   const int h = lane >> 5;
 
-  const Work wk = decode_work<MODE>(p, qred, wave, lane);
+  const Work wk = decode_work<MODE, kWaves, SP>(p, qred, wave, lane);
   const int b = wk.b, hk = wk.hk, split = wk.split;
   const bool valid = wk.valid;
   const int64_t qrow_idx = wk.qrow_idx;
@@ -857,6 +937,20 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
           const int key = k2 * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
           if (kp[key] > qpos) s[k2][r] = -INFINITY;
         }
+      if constexpr (SP) {
+        // block mask: the lane's query block row, one bit per key block
+        const uint32_t* row = p.sp_bits + (int64_t)(wk.spos >> p.sp_lgq) * p.sp_rw;
+#pragma unroll
+        for (int k2 = 0; k2 < BN / 32; ++k2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kpos = kp[k2 * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+            if (kpos != kPosNone) {
+              const int kb = kpos >> p.sp_lgk;
+              if (!((row[kb >> 5] >> (kb & 31)) & 1u)) s[k2][r] = -INFINITY;
+            }
+          }
+      }
     }
     float mt = -INFINITY;
 #pragma unroll
@@ -892,7 +986,16 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
 
   // K and V of a tile are staged together; the tile after is fetched from HBM
   // into registers while this one is computed.
-  TileInfo cur = next_tile<MODE, ELEM>(p, tbeg, 0, tend, gqmax, b, hk);
+  SparseWalk sw = {nullptr, 0};
+  int e0 = 0;
+  if constexpr (SP) {
+    sw.list = p.sp_list + (int64_t)wk.qt * p.sp_cap;
+    const int cnt = p.sp_count[wk.qt];
+    e0 = lower_entry(sw.list, cnt, tbeg);
+    sw.end = lower_entry(sw.list, cnt, tend);
+  }
+  TileInfo cur = SP ? sparse_tile<MODE, ELEM>(p, sw, e0, 0, tend, gqmax, b, hk)
+                    : next_tile<MODE, ELEM>(p, tbeg, 0, tend, gqmax, b, hk);
   if (cur.t < tend) {
     O::template fetch_k<MODE>(p, cur, b, hk, tid, sk);
     O::template fetch_v<MODE>(p, cur, b, hk, tid, sv);
@@ -901,13 +1004,15 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(Params p) {
   }
   int bi = 0;
   while (cur.t < tend) {
-    const TileInfo nxt = successor<MODE, ELEM>(p, cur, tend, gqmax, b, hk);
+    const TileInfo nxt = SP ? sparse_successor<MODE, ELEM>(p, sw, cur, tend, gqmax, b, hk)
+                            : successor<MODE, ELEM>(p, cur, tend, gqmax, b, hk);
     if (nxt.t < tend) {
       O::template fetch_k<MODE>(p, nxt, b, hk, tid, sk);
       O::template fetch_v<MODE>(p, nxt, b, hk, tid, sv);
     }
     __syncthreads();  // K(cur) and V(cur) are in LDS
-    const int mode = wave_mode(cur, wqmin, wqmax, MODE == kRingCausal);
+    int mode = wave_mode(cur, wqmin, wqmax, MODE == kRingCausal);
+    if (SP && mode == 1) mode = 2;  // the block mask is checked per score
     if (mode) {
       // Raised priority while issuing matrix ops: of the two waves sharing a
       // SIMD, the one with MFMAs ready goes first and the other fills VALU slots.
@@ -1109,7 +1214,12 @@ constexpr int vmcnt_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
 // selects the variant that applies it to every tile (1: kps = 1; 2: any kps,
 // at the cost of an fp64 multiply per lane and step); with MASK = 0 no
 // tile needs one (no causal mask and a whole number of tiles).
-template <int DP, int MODE, int MASK>
+//
+// SP (block-sparse calls, MASK = 1): the tiles come from the work item's list,
+// and every row of a wave lies in one query block while a tile spans at most
+// two key blocks, so the block mask admits one run [lo, hi] of each tile's keys
+// per wave; lo joins the per-lane upper bound above.
+template <int DP, int MODE, int MASK, bool SP = false>
 __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void attention_bf16_kernel(Params p) {
   constexpr int W = pipe_waves(MODE);
   constexpr int kPipeThreads = 64 * W;
@@ -1138,9 +1248,11 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
 
-  const Work wk = decode_work<MODE, W>(p, qred, wave, lane);
+  const Work wk = decode_work<MODE, W, SP>(p, qred, wave, lane);
   const int b = wk.b, hk = wk.hk;
   const typename O::Lanes L = O::lanes(lane);
+  // block-sparse calls: the wave's query block (the same for all its rows)
+  const int wqb = SP ? __builtin_amdgcn_readfirstlane(wk.valid ? wk.spos >> p.sp_lgq : 0) : 0;
 
   typename O::QFrag qf;
   O::load_q(p, (const __bf16*)p.q + wk.qrow_idx * p.d, wk.valid, h, qf);
@@ -1334,12 +1446,43 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
     if constexpr (MASK == 2) rel = rel < 0 ? -1 : (int)__builtin_fma((double)rel, p.kinv, 0.5 * p.kinv);
     return min(rel, nvalid - 1) - 4 * h;
   };
-  auto mask_tile = [&](f32x16* s, int bound) {
+  // Keys outside [lo, bound] (both minus 4h) are masked; lo only on block-sparse calls.
+  auto mask_tile = [&](f32x16* s, int bound, int lo) {
 #pragma unroll
     for (int k2 = 0; k2 < TB / 32; ++k2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (k2 * 32 + 8 * (r >> 2) + (r & 3) > bound) s[k2][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int key = k2 * 32 + 8 * (r >> 2) + (r & 3);
+        if (key > bound || (SP && key < lo)) s[k2][r] = -INFINITY;
+      }
+  };
+  // Block-sparse calls: the run of keys of the tile starting at position pos0
+  // that the block mask admits for this wave, packed as (lo << 16) | (hi + 1)
+  // (empty: lo = TB, hi = -1). The tile's keys are pos0 .. pos0 + TB - 1 and
+  // key blocks are at least TB long, so the tile meets blocks kb0 and kb0 + 1.
+  auto sparse_run = [&](int pos0) {
+    if constexpr (!SP) {
+      return (int)TB;
+    } else {
+      const int kb0 = pos0 >> p.sp_lgk;
+      const uint32_t* row = p.sp_bits + (int64_t)wqb * p.sp_rw + (kb0 >> 5);
+      const uint32_t w0 = cload(row), w1 = cload(row + 1);
+      const int sh = kb0 & 31;
+      const bool b0 = (w0 >> sh) & 1u;
+      const bool b1 = sh == 31 ? (w1 & 1u) : ((w0 >> (sh + 1)) & 1u);
+      const int split = ((kb0 + 1) << p.sp_lgk) - pos0;  // first key of block kb0 + 1
+      int lo = TB, hi = -1;
+      if (split >= TB) {
+        if (b0) lo = 0, hi = TB - 1;
+      } else if (b0 && b1) {
+        lo = 0, hi = TB - 1;
+      } else if (b0) {
+        lo = 0, hi = split - 1;
+      } else if (b1) {
+        lo = split, hi = TB - 1;
+      }
+      return (lo << 16) | (hi + 1);
+    }
   };
 
   uint32_t off[O::NS];
@@ -1369,26 +1512,45 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
 
-  const TileInfo t0 = uniform(next_tile<MODE, 2, TB>(p, tbeg, 0, tend, wk.gqmax, b, hk));
+  // the work item's tiles: the dense walk, or entries of its list on block-sparse calls
+  SparseWalk sw = {nullptr, 0};
+  int e0 = 0;
+  if constexpr (SP) {
+    sw.list = p.sp_list + (int64_t)wk.qt * p.sp_cap;
+    const int cnt = cload(p.sp_count + wk.qt);
+    e0 = lower_entry(sw.list, cnt, tbeg);
+    sw.end = lower_entry(sw.list, cnt, tend);
+  }
+  auto next_of = [&](const TileInfo& x) {
+    if constexpr (SP)
+      return uniform(sparse_successor<MODE, 2, TB>(p, sw, x, tend, wk.gqmax, b, hk));
+    else
+      return uniform(successor<MODE, 2, TB>(p, x, tend, wk.gqmax, b, hk));
+  };
+  const TileInfo t0 = SP ? uniform(sparse_tile<MODE, 2, TB>(p, sw, e0, 0, tend, wk.gqmax, b, hk))
+                         : uniform(next_tile<MODE, 2, TB>(p, tbeg, 0, tend, wk.gqmax, b, hk));
   if (t0.t < tend) {
     f32x16 sa[TB / 32], sb[TB / 32];
-    // Tile index and first position of tiles j .. j+D, in slot (tile mod NB).
-    int qt[NB], qp[NB];
+    // Tile index and first position of tiles j .. j+D, in slot (tile mod NB),
+    // and (block-sparse calls) the run of keys the block mask admits.
+    int qt[NB], qp[NB], qm[NB];
 
     // Prologue: K(0), then groups {K(k+1), V(k)} for k < D.
     qt[0] = t0.t;
     qp[0] = t0.pos0;
+    qm[0] = sparse_run(t0.pos0);
     stage(t0, false, kbuf[0]);
     TileInfo tv = t0;
-    TileInfo tk = uniform(successor<MODE, 2, TB>(p, t0, tend, wk.gqmax, b, hk));
+    TileInfo tk = next_of(t0);
 #pragma unroll
     for (int k = 0; k < D; ++k) {
       qt[k + 1] = tk.t;
       qp[k + 1] = tk.pos0;
+      qm[k + 1] = sparse_run(tk.pos0);
       if (tk.t < tend) stage(tk, false, kbuf[k + 1]);
       if (tv.t < tend) stage(tv, true, vbuf[k]);
       tv = tk;
-      if (tk.t < tend) tk = uniform(successor<MODE, 2, TB>(p, tk, tend, wk.gqmax, b, hk));
+      if (tk.t < tend) tk = next_of(tk);
     }
     // K(0) has landed once at most the D groups after it are in flight.
     if (qt[D] < tend)
@@ -1397,7 +1559,14 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
     O::qk(kbuf[0], qf, L, sa);
-    if constexpr (MASK) mask_tile(sa, key_bound(qt[0], qp[0]));
+    if constexpr (MASK) {
+      int hi = key_bound(qt[0], qp[0]), lo = 0;
+      if constexpr (SP) {
+        hi = min(hi, (qm[0] & 0xffff) - 1 - 4 * h);
+        lo = (qm[0] >> 16) - 4 * h;
+      }
+      mask_tile(sa, hi, lo);
+    }
     float mt = lane_max(sa);  // lane maximum of the scores of the next tile to exponentiate
 
     // Iteration j (BI = j mod NB): scores of tile j in sc, of tile j+1 into sn.
@@ -1406,8 +1575,8 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
     // The four ring buffers of a step are passed as restrict pointers: the
     // compiler then knows that the reads of K(j+1) and V(j) do not touch the
     // buffers being filled, and does not make them wait for those copies.
-    auto step_body = [&](f32x16* sc, f32x16* sn, auto bi_c, auto mask_c, int bound, char* __restrict__ k_fill,
-                         char* __restrict__ v_fill, const char* __restrict__ k_read,
+    auto step_body = [&](f32x16* sc, f32x16* sn, auto bi_c, auto mask_c, int bound, int lo, bool lo_any,
+                         char* __restrict__ k_fill, char* __restrict__ v_fill, const char* __restrict__ k_read,
                          const char* __restrict__ v_read) {
       constexpr int BI = decltype(bi_c)::value;
       constexpr bool MASKED = decltype(mask_c)::value != 0;
@@ -1417,6 +1586,7 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
       rescale_o();           // o to that reference
       qt[BI] = tk.t;
       qp[BI] = tk.pos0;
+      if constexpr (SP) qm[BI] = sparse_run(tk.pos0);
       if (tk.t < tend) stage(tk, false, k_fill);  // K(j+1+D)
       if (tv.t < tend) stage(tv, true, v_fill);   // V(j+D)
       __builtin_amdgcn_sched_barrier(0);
@@ -1428,17 +1598,26 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
       // some lane of the wave cannot see every key of tile j+1 (its highest key
       // index in a lane is TB - 5 + 4h): mask, and take the maximum again (the
       // masked maximum never exceeds the one above)
-      if (MASKED && __any(bound < TB - 5)) {
-        mask_tile(sn, bound);
+      if (MASKED && (__any(bound < TB - 5) || (SP && lo_any))) {
+        mask_tile(sn, bound, lo);
         mt = fminf(mt, lane_max(sn));
       }
       tv = tk;
-      if (tk.t < tend) tk = uniform(successor<MODE, 2, TB>(p, tk, tend, wk.gqmax, b, hk));
+      if (tk.t < tend) tk = next_of(tk);
     };
     auto step = [&](f32x16* sc, f32x16* sn, auto bi_c) {
       constexpr int BI = decltype(bi_c)::value;
-      const int bound = MASK ? key_bound(qt[(BI + 1) % NB], qp[(BI + 1) % NB]) : 0;
-      step_body(sc, sn, bi_c, IntC<MASK>{}, bound, kbuf[BI], vbuf[(BI + D) % NB], kbuf[(BI + 1) % NB], vbuf[BI]);
+      int bound = MASK ? key_bound(qt[(BI + 1) % NB], qp[(BI + 1) % NB]) : 0;
+      int lo = 0;
+      bool lo_any = false;
+      if constexpr (SP) {
+        const int m = qm[(BI + 1) % NB];
+        bound = min(bound, (m & 0xffff) - 1 - 4 * h);
+        lo = (m >> 16) - 4 * h;
+        lo_any = (m >> 16) > 0;
+      }
+      step_body(sc, sn, bi_c, IntC<MASK>{}, bound, lo, lo_any, kbuf[BI], vbuf[(BI + D) % NB], kbuf[(BI + 1) % NB],
+                vbuf[BI]);
     };
 
     while (true) {
@@ -1578,6 +1757,117 @@ __global__ __launch_bounds__(256) void merge_kernel(int64_t rows, int d, int lpr
       al[r] = la * fa + lb * fb;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Block-sparse planning. The caller's mask is a byte matrix over (query block,
+// key block) of global positions. sparse_bits_kernel packs it 32 key blocks per
+// word (row stride rw words, the last word of a row zero, so a two-word read
+// at any key block of the row stays inside it). sparse_plan_kernel then lists,
+// for each query tile of bm rows, the key tiles of tb keys that hold at least
+// one pair the mask (and, when causal, the positions) allow, in ascending
+// order. Position runs with a step other than 1 are treated as their whole
+// interval, which can only add tiles, never drop one.
+
+__global__ __launch_bounds__(256) void sparse_bits_kernel(const uint8_t* __restrict__ mask, int64_t nqb, int64_t nkb,
+                                                          int rw, uint32_t* __restrict__ words) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nqb * rw) return;
+  const int64_t a = i / rw;
+  const int64_t kb0 = (i % rw) * 32;
+  uint32_t bits = 0;
+  for (int j = 0; j < 32; ++j)
+    if (kb0 + j < nkb && mask[a * nkb + kb0 + j] != 0) bits |= 1u << j;
+  words[i] = bits;
+}
+
+constexpr int kPlanParts = 8;  // query position runs kept per query tile (more are merged into the last)
+
+// Is some pair of a query in [qlo, qhi] and a key in [klo, khi] allowed?
+__device__ __forceinline__ bool runs_meet(const uint32_t* __restrict__ words, int rw, int lgq, int lgk, bool causal,
+                                          int qlo, int qhi, int klo, int khi) {
+  if (causal && klo > qhi) return false;
+  const int qa = qlo >> lgq, qz = qhi >> lgq, ka = klo >> lgk, kz = khi >> lgk;
+  if ((int64_t)(qz - qa + 1) * (kz - ka + 1) > 4096) return true;  // too many blocks to check: keep the tile
+  for (int qb = qa; qb <= qz; ++qb) {
+    const uint32_t* row = words + (int64_t)qb * rw;
+    const int64_t qmax = min((int64_t)qhi, (((int64_t)qb + 1) << lgq) - 1);
+    for (int kb = ka; kb <= kz; ++kb) {
+      if (!((row[kb >> 5] >> (kb & 31)) & 1u)) continue;
+      if (!causal || max((int64_t)klo, (int64_t)kb << lgk) <= qmax) return true;
+    }
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(256) void sparse_plan_kernel(const ChunkDev* __restrict__ chunks, int n_chunks,
+                                                          const QSegDev* __restrict__ qsegs, int n_qseg, int64_t lq,
+                                                          int64_t lk, int bm, int tb, const uint32_t* __restrict__ words,
+                                                          int rw, int lgq, int lgk, int causal, int cap,
+                                                          int* __restrict__ list, int* __restrict__ count) {
+  __shared__ int qlo_s[kPlanParts], qhi_s[kPlanParts];
+  __shared__ int nparts_s;
+  __shared__ int wsum[4];
+  const int qt = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    // position runs of this query tile's rows, one per query segment it meets
+    int np = 0;
+    const int64_t r0 = (int64_t)qt * bm, r1 = min(lq, r0 + bm);
+    for (int s = 0; s < n_qseg; ++s) {
+      const QSegDev g = qsegs[s];
+      const int64_t a = max(r0, g.row0), e = min(r1, g.row0 + g.len);
+      if (a >= e) continue;
+      const int lo = (int)(g.pos0 + g.ps * (a - g.row0)), hi = (int)(g.pos0 + g.ps * (e - 1 - g.row0));
+      if (np < kPlanParts) {
+        qlo_s[np] = lo;
+        qhi_s[np] = hi;
+        ++np;
+      } else {
+        qlo_s[np - 1] = min(qlo_s[np - 1], lo);
+        qhi_s[np - 1] = max(qhi_s[np - 1], hi);
+      }
+    }
+    nparts_s = np;
+  }
+  __syncthreads();
+  const int np = nparts_s;
+  const int ntiles = (int)((lk + tb - 1) / tb);
+  const int wave = tid >> 6, lane = tid & 63;
+  int running = 0;
+  for (int base = 0; base < ntiles; base += 256) {
+    const int t = base + tid;
+    bool vis = false;
+    if (t < ntiles) {
+      int64_t j0 = (int64_t)t * tb;
+      const int64_t j1 = min(lk, j0 + tb);
+      int lo = 0, hi = n_chunks - 1;  // last chunk starting at or before key j0
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunks[mid].start <= j0) lo = mid; else hi = mid - 1;
+      }
+      for (int c = lo; j0 < j1 && c < n_chunks && !vis; ++c) {
+        const ChunkDev ch = chunks[c];
+        const int64_t e = min(j1, ch.start + ch.len);
+        if (e <= j0) continue;
+        const int klo = ch.pos0 + ch.ps * (int)(j0 - ch.start), khi = ch.pos0 + ch.ps * (int)(e - 1 - ch.start);
+        for (int i = 0; i < np && !vis; ++i)
+          vis = runs_meet(words, rw, lgq, lgk, causal != 0, qlo_s[i], qhi_s[i], klo, khi);
+        j0 = e;
+      }
+    }
+    // compact in tile order: ballot within each wave, wave totals through LDS
+    const uint64_t bal = __ballot(vis);
+    const int before = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = running;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (vis) list[(int64_t)qt * cap + off + before] = t;
+    running += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (tid == 0) count[qt] = running;
 }
 
 }  // namespace
@@ -1730,6 +2020,27 @@ hipError_t launch(int mode, int dtype, int dp, const Params& p, bool pipe, bool 
   if (mode == kStats) return launch_mode<kStats>(dtype, dp, p, nblocks, s);
   if (mode == kRingFull) return launch_mode<kRingFull>(dtype, dp, p, nblocks, s);
   return launch_mode<kRingCausal>(dtype, dp, p, nblocks, s);
+}
+
+// Block-sparse variants: the pipelined kernel (MASK = 1 with the block run) or
+// the general kernel with the per-score block check.
+template <int DP, int MODE>
+hipError_t launch_sparse_dp(int dtype, bool pipe, const Params& p, int nblocks, hipStream_t s) {
+  if (pipe)
+    hipLaunchKernelGGL((attention_bf16_kernel<DP, MODE, 1, true>), dim3(nblocks), dim3(64 * pipe_waves(MODE)), 0, s,
+                       p);
+  else if (dtype == RA_BF16)
+    hipLaunchKernelGGL((attention_kernel<__bf16, DP, MODE, true>), dim3(nblocks), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((attention_kernel<float, DP, MODE, true>), dim3(nblocks), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_sparse_mode(int dtype, int dp, bool pipe, const Params& p, int nblocks, hipStream_t s) {
+  if (dp == 32) return launch_sparse_dp<32, MODE>(dtype, pipe, p, nblocks, s);
+  if (dp == 64) return launch_sparse_dp<64, MODE>(dtype, pipe, p, nblocks, s);
+  return launch_sparse_dp<128, MODE>(dtype, pipe, p, nblocks, s);
 }
 
 
@@ -2054,12 +2365,64 @@ int scratch_address(void** out) {
   return RA_OK;
 }
 
+// Block mask of a block-sparse call (see ra_ring_attention_block_sparse).
+struct SparseSpec {
+  const uint8_t* mask;  // device, [nqb][nkb]
+  int64_t nqb, nkb;
+  int64_t bq, bk;       // block sizes in positions (powers of two)
+};
+
+int log2_exact(int64_t x) {
+  int l = 0;
+  while (((int64_t)1 << l) < x) ++l;
+  return ((int64_t)1 << l) == x ? l : -1;
+}
+
+// Rows of the block-sparse workspace beyond the ring call's own: the packed
+// mask, and per query tile a tile count and a list of key tiles (sized for the
+// general kernel's 128-row query tiles and 64-key tiles, the larger counts).
+struct SparseLayout {
+  int rw;              // words per packed mask row
+  int64_t nqt, cap;    // query tiles and list row length provided for
+  size_t bits, count, list, total;
+};
+
+SparseLayout sparse_layout(size_t base, int64_t q_len, int64_t total_keys, int64_t nqb, int64_t nkb) {
+  SparseLayout L;
+  L.rw = (int)((nkb + 31) / 32) + 1;
+  L.nqt = (q_len + BM - 1) / BM;
+  L.cap = (total_keys + BN - 1) / BN;
+  L.bits = base;
+  L.count = L.bits + align256(sizeof(uint32_t) * (size_t)nqb * (size_t)L.rw);
+  L.list = L.count + align256(sizeof(int) * (size_t)(L.nqt > 0 ? L.nqt : 1));
+  L.total = L.list + align256(sizeof(int) * (size_t)L.nqt * (size_t)(L.cap > 0 ? L.cap : 1));
+  return L;
+}
+
+// True when every 32-row group of query rows (a wave of the pipelined kernel)
+// lies in one query block of 2^lgq positions.
+bool waves_in_one_qblock(const ra_q_segment* segs, int n, int lgq) {
+  int64_t row = 0, wave_qb = -1;
+  for (int s = 0; s < n; ++s) {
+    const int64_t step = pos_step(segs[s].pos_stride);
+    for (int64_t i = 0; i < segs[s].len; ++i, ++row) {
+      const int64_t qb = (segs[s].global_offset + step * i) >> lgq;
+      if ((row & 31) == 0)
+        wave_qb = qb;
+      else if (qb != wave_qb)
+        return false;
+    }
+  }
+  return true;
+}
+
 // The ring call. With use_scratch the workspace is the device's `scratch`
-// array (workspace and workspace_bytes are ignored).
+// array (workspace and workspace_bytes are ignored). With sp, the block mask
+// restricts the visible keys as well.
 int ring_attention_call(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
                         const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks, int n_chunks,
                         int causal, float scale, void* workspace, size_t workspace_bytes, bool use_scratch,
-                        float* out, float* lse, void* stream) {
+                        const SparseSpec* sp, float* out, float* lse, void* stream) {
   g_err[0] = 0;
   int st = check_dims(dtype, batch, q_heads, kv_heads, head_dim);
   if (st) return st;
@@ -2072,7 +2435,7 @@ int ring_attention_call(int dtype, int batch, int q_heads, int kv_heads, int hea
     const ra_q_segment& g = q_segments[s];
     if (g.len < 0) return fail(RA_ERR_SHAPE, "query segment %d: negative length", s);
     if (g.pos_stride < 0) return fail(RA_ERR_SHAPE, "query segment %d: negative pos_stride", s);
-    if (causal && g.len > 0 && !positions_fit(g.global_offset, g.len, pos_step(g.pos_stride)))
+    if ((causal || sp) && g.len > 0 && !positions_fit(g.global_offset, g.len, pos_step(g.pos_stride)))
       return fail(RA_ERR_SHAPE, "query segment %d: positions outside [0, 2^31-1)", s);
     lq += g.len;
   }
@@ -2085,11 +2448,38 @@ int ring_attention_call(int dtype, int batch, int q_heads, int kv_heads, int hea
     vec = vec && chunk_vec_ok(chunks[c], head_dim, elem);
   }
   if (lk > kPosLimit) return fail(RA_ERR_UNSUPPORTED, "more than 2^31-2 keys in total");
+  int lgq = 0, lgk = 0;
+  if (sp) {
+    lgq = log2_exact(sp->bq);
+    lgk = log2_exact(sp->bk);
+    if (lgq < 0 || lgk < 0 || lgq > 30 || lgk > 30)
+      return fail(RA_ERR_SHAPE, "block sizes %lld x %lld must be powers of two up to 2^30", (long long)sp->bq,
+                  (long long)sp->bk);
+    if (sp->nqb < 1 || sp->nkb < 1 || sp->nqb > (1LL << 31) || sp->nkb > (1LL << 31))
+      return fail(RA_ERR_SHAPE, "block mask of %lld x %lld blocks", (long long)sp->nqb, (long long)sp->nkb);
+    for (int s = 0; s < n_q_segments; ++s) {
+      const ra_q_segment& g = q_segments[s];
+      if (g.len > 0 && (g.global_offset + pos_step(g.pos_stride) * (g.len - 1)) >> lgq >= sp->nqb)
+        return fail(RA_ERR_SHAPE, "query segment %d reaches past the block mask's %lld query blocks", s,
+                    (long long)sp->nqb);
+    }
+    for (int c = 0; c < n_chunks; ++c) {
+      const ra_kv_chunk& ch = chunks[c];
+      if (ch.len > 0 && (ch.global_offset + pos_step(ch.pos_stride) * (ch.len - 1)) >> lgk >= sp->nkb)
+        return fail(RA_ERR_SHAPE, "chunk %d reaches past the block mask's %lld key blocks", c, (long long)sp->nkb);
+    }
+  }
   if (lq == 0 || batch == 0) return RA_OK;
   if (!q || !out) return fail(RA_ERR_NULL, "q and out must be non-null");
+  if (sp && lk > 0 && !sp->mask) return fail(RA_ERR_NULL, "block mask is null");
   int kps = 1;
-  const bool pipe = pipe_ok(dtype, head_dim, vec && vec_ok(q, head_dim, head_dim, elem), chunks, n_chunks,
-                            causal != 0, &kps);
+  const bool vecq = vec && vec_ok(q, head_dim, head_dim, elem);
+  // block-sparse calls take the pipelined kernel when each wave's rows share a query block, the keys of a
+  // tile are consecutive positions and a tile meets at most two key blocks; else the general kernel
+  const bool pipe = sp ? (pipe_ok(dtype, head_dim, vecq, chunks, n_chunks, true, &kps) && kps == 1 &&
+                          sp->bk >= pipe_tile(dp_of(head_dim)) && waves_in_one_qblock(q_segments, n_q_segments, lgq))
+                       : pipe_ok(dtype, head_dim, vecq, chunks, n_chunks, causal != 0, &kps);
+  if (sp) kps = 1;
   const int bm = pipe ? pipe_bm(kRingFull) : BM;
   const int64_t n_qt = (lq + bm - 1) / bm;
   const int64_t base_blocks = n_qt * q_heads * batch;
@@ -2100,8 +2490,9 @@ int ring_attention_call(int dtype, int batch, int q_heads, int kv_heads, int hea
   const size_t tbytes = table_bytes(n_chunks, n_q_segments);
   // the public size covers either kernel's key-range cut; the static scratch only needs the bytes this
   // call uses: its tables and the partials of the cut it runs with
-  const size_t need = use_scratch ? tbytes + partial_bytes(nsplit, rows, head_dim)
-                                  : ra_ring_workspace_bytes(batch, q_heads, head_dim, lq, lk, n_chunks, n_q_segments);
+  const size_t ring_bytes = ra_ring_workspace_bytes(batch, q_heads, head_dim, lq, lk, n_chunks, n_q_segments);
+  const SparseLayout SL = sp ? sparse_layout(ring_bytes, lq, lk, sp->nqb, sp->nkb) : SparseLayout{};
+  const size_t need = use_scratch ? tbytes + partial_bytes(nsplit, rows, head_dim) : (sp ? SL.total : ring_bytes);
   if (use_scratch) {
     if (need > kScratchBytes)
       return fail(RA_ERR_WORKSPACE, "this share needs %zu bytes of workspace; the static scratch holds %zu", need,
@@ -2174,8 +2565,36 @@ int ring_attention_call(int dtype, int batch, int q_heads, int kv_heads, int hea
   p.scale = scale;
   p.c2 = scale * kLog2e;
   const bool mask = causal || lk % pipe_tile(dp_of(head_dim)) != 0;
+  if (sp && lk > 0) {
+    // pack the mask, then list each query tile's key tiles that hold an allowed pair
+    char* ws = (char*)workspace;
+    const int tb = pipe ? pipe_tile(dp_of(head_dim)) : BN;
+    p.sp_bits = (const uint32_t*)(ws + SL.bits);
+    p.sp_count = (const int*)(ws + SL.count);
+    p.sp_list = (const int*)(ws + SL.list);
+    p.sp_cap = (int)((lk + tb - 1) / tb);
+    p.sp_rw = SL.rw;
+    p.sp_lgq = lgq;
+    p.sp_lgk = lgk;
+    const int64_t nwords = sp->nqb * SL.rw;
+    hipLaunchKernelGGL(sparse_bits_kernel, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, hs, sp->mask,
+                       sp->nqb, sp->nkb, SL.rw, (uint32_t*)(ws + SL.bits));
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "ring_attention_block_sparse mask packing launch");
+    hipLaunchKernelGGL(sparse_plan_kernel, dim3((unsigned)n_qt), dim3(256), 0, hs, p.chunks, nc, p.qsegs,
+                       n_q_segments, lq, lk, bm, tb, p.sp_bits, SL.rw, lgq, lgk, causal ? 1 : 0, p.sp_cap,
+                       (int*)(ws + SL.list), (int*)(ws + SL.count));
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "ring_attention_block_sparse plan launch");
+  }
   timer_begin(hs);
-  e = launch(causal ? kRingCausal : kRingFull, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, hs);
+  if (sp && lk > 0) {
+    const int md = causal ? kRingCausal : kRingFull;
+    e = md == kRingCausal ? launch_sparse_mode<kRingCausal>(dtype, dp_of(head_dim), pipe, p, (int)nblocks, hs)
+                          : launch_sparse_mode<kRingFull>(dtype, dp_of(head_dim), pipe, p, (int)nblocks, hs);
+  } else {
+    e = launch(causal ? kRingCausal : kRingFull, dtype, dp_of(head_dim), p, pipe, mask, (int)nblocks, hs);
+  }
   timer_end(hs);
   if (e != hipSuccess) return hip_fail(e, "ring_attention launch");
   if (nsplit > 1) {
@@ -2194,14 +2613,34 @@ int ra_ring_attention(int dtype, int batch, int q_heads, int kv_heads, int head_
                       int causal, float scale, void* workspace, size_t workspace_bytes, float* out, float* lse,
                       void* stream) {
   return ring_attention_call(dtype, batch, q_heads, kv_heads, head_dim, q, q_segments, n_q_segments, chunks,
-                             n_chunks, causal, scale, workspace, workspace_bytes, false, out, lse, stream);
+                             n_chunks, causal, scale, workspace, workspace_bytes, false, nullptr, out, lse, stream);
+}
+
+size_t ra_block_sparse_workspace_bytes(int batch, int q_heads, int head_dim, int64_t q_len, int64_t total_keys,
+                                       int n_chunks, int n_q_segments, int64_t n_qblocks, int64_t n_kblocks) {
+  if (q_len < 0) q_len = 0;
+  if (total_keys < 0) total_keys = 0;
+  if (n_qblocks < 1) n_qblocks = 1;
+  if (n_kblocks < 1) n_kblocks = 1;
+  const size_t base = ra_ring_workspace_bytes(batch, q_heads, head_dim, q_len, total_keys, n_chunks, n_q_segments);
+  return sparse_layout(base, q_len, total_keys, n_qblocks, n_kblocks).total;
+}
+
+int ra_ring_attention_block_sparse(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
+                                   const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks,
+                                   int n_chunks, int causal, float scale, const uint8_t* block_mask,
+                                   int64_t n_qblocks, int64_t n_kblocks, int64_t block_q, int64_t block_k,
+                                   void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+  const SparseSpec sp = {block_mask, n_qblocks, n_kblocks, block_q, block_k};
+  return ring_attention_call(dtype, batch, q_heads, kv_heads, head_dim, q, q_segments, n_q_segments, chunks,
+                             n_chunks, causal, scale, workspace, workspace_bytes, false, &sp, out, lse, stream);
 }
 
 int ra_ring_attention_noalloc(int dtype, int batch, int q_heads, int kv_heads, int head_dim, const void* q,
                               const ra_q_segment* q_segments, int n_q_segments, const ra_kv_chunk* chunks,
                               int n_chunks, int causal, float scale, float* out, float* lse, void* stream) {
   return ring_attention_call(dtype, batch, q_heads, kv_heads, head_dim, q, q_segments, n_q_segments, chunks,
-                             n_chunks, causal, scale, nullptr, 0, true, out, lse, stream);
+                             n_chunks, causal, scale, nullptr, 0, true, nullptr, out, lse, stream);
 }
 
 }  // extern "C"

@@ -132,6 +132,28 @@ def test_noalloc_refuses_a_share_beyond_its_scratch(lib):
     assert lib.ra_ring_attention_noalloc(1, 1, 8, 1, 128, FAKE, seg, 1, ch, 1, 0, 0.1, None, None, None) == 1
 
 
+def test_block_sparse_validation(lib):
+    """Host-side checks only: block sizes, mask extent against every position, and the mask pointer."""
+    seg = (api.QSegment * 1)(api.QSegment(64, 128))
+    ch = (api.KVChunk * 2)(api.KVChunk(FAKE, FAKE, 256, 0, 0, 0, 64), api.KVChunk(FAKE, FAKE, 256, 256, 0, 0, 64))
+    need = lib.ra_block_sparse_workspace_bytes(1, 2, 64, 64, 512, 2, 1, 4, 4)
+    assert need % 256 == 0 and need > lib.ra_ring_workspace_bytes(1, 2, 64, 64, 512, 2, 1)
+
+    def call(mask=FAKE, nqb=4, nkb=4, bq=128, bk=128, causal=0, ws=None, wsb=0):
+        return lib.ra_ring_attention_block_sparse(1, 1, 2, 2, 64, FAKE, seg, 1, ch, 2, causal, 0.125, mask, nqb, nkb,
+                                                  bq, bk, ws, wsb, FAKE, None, None)
+
+    assert call(bq=96) == 2  # not a power of two
+    assert call(bk=0) == 2
+    assert call(nqb=1) == 2  # queries at 128..191 lie in query block 1
+    assert b"query segment" in lib.ra_last_error()
+    assert call(nkb=3) == 2  # keys reach position 511, key block 3
+    assert b"chunk" in lib.ra_last_error()
+    assert call(mask=None) == 1
+    assert call() == 6  # all valid: fails on the missing workspace
+    assert call(ws=ctypes.c_void_p(0x1000), wsb=need - 256) == 6
+
+
 def test_empty_work_is_a_no_op(lib):
     seg = (api.QSegment * 1)(api.QSegment(0, 0))
     assert _ring(lib, segs=seg) == 0  # no queries: nothing to launch
