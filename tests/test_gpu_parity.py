@@ -239,6 +239,23 @@ def test_chunk_stats_small(dtype, d):
     _check_lse(np.log(_np(l)) + _np(m), np.log(rl) + rm, dtype, 333)
 
 
+@pytest.mark.parametrize("d,nk", [(64, 100), (64, 129), (64, 640), (32, 127), (32, 300), (64, 4096 + 77)])
+def test_chunk_stats_key_halves(d, nk):
+    """At head_dim <= 64 a chunk-statistics workgroup walks the first and the second half of the key tiles in
+    two halves and merges them: one tile (the second half empty), two, an odd count with a ragged end, and a
+    long chunk; 600 query rows over 4 heads so that several workgroups and a partial one run."""
+    _say(f"chunk_stats halves d={d} keys={nk}")
+    w = wl.custom("sthalves", "bf16", 1, 4, 2, d, [(0, 600)], [(0, nk)], False, seed=d * 7 + nk)
+    q, k, v, kc, vc = wl.generate_torch(w, DEV)
+    u, l, m = ra.attention_chunk_stats(q, kc[0], vc[0], workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    ru, rl, rm = oracle.chunk_stats(q.cpu(), np.repeat(kc[0].cpu().float().numpy(), 2, axis=1),
+                                    np.repeat(vc[0].cpu().float().numpy(), 2, axis=1), 1 / math.sqrt(d))
+    _check(_np(u) / _np(l)[..., None], ru / rl[..., None], "bf16")
+    assert np.abs(_np(m) - rm).max() <= 1e-4 * max(1, np.abs(rm).max())
+    _check_lse(np.log(_np(l)) + _np(m), np.log(rl) + rm, "bf16", nk)
+
+
 @pytest.mark.parametrize("dtype,d,nk", [("bf16", 64, 4096), ("bf16", 128, 4096), ("f32", 32, 2048)])
 def test_chunk_stats_key_range_split(dtype, d, nk):
     """Few query rows against a long chunk: the keys are cut into ranges and the partial statistics
