@@ -60,6 +60,8 @@ def parse():
                     help="turn a rocprofv3 --kernel-trace --stats run of this script and the JSON line it printed "
                          "into a profiles/ summary")
     ap.add_argument("--command", default="", help="with --summarize-*: the command lines that made the files")
+    ap.add_argument("--with-backward", action="store_true",
+                    help="with --profile-run: also run the backward pass of the workload")
     return ap.parse_args()
 
 
@@ -454,6 +456,16 @@ def profile_run(args):
         ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
                           kv_position_strides=w.kv_strides)
     torch.cuda.synchronize()
+    if args.with_backward:
+        out, lse = ra.ring_attention(q, kc, vc, w.q_runs, offs, causal=w.causal, scale=w.softmax_scale,
+                                     return_lse=True, kv_position_strides=w.kv_strides)
+        g = torch.Generator(device=dev).manual_seed(7)
+        dout = torch.randn(q.shape, device=dev, generator=g).to(torch.bfloat16)
+        for _ in range(args.warmup + args.steps):
+            ra.ring_attention_backward(q, kc, vc, out, lse, dout, w.q_runs, offs, causal=w.causal,
+                                       scale=w.softmax_scale, kv_position_strides=w.kv_strides)
+        torch.cuda.synchronize()
+        del out, lse, dout
     del q, k, v, kc, vc
     # calibration: an elementwise kernel that reads COPY_BYTES and writes COPY_BYTES
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -563,14 +575,25 @@ def summarize_pmc(args):
     }
     if len(dirs) == 4:
         ins = _counter_rows(dirs[3])
-        valu, _ = _per_dispatch(ins, attn_name, "SQ_INSTS_VALU")
-        mfma, _ = _per_dispatch(ins, attn_name, "SQ_INSTS_MFMA")
-        lds, _ = _per_dispatch(ins, attn_name, "SQ_INSTS_LDS")
-        salu, _ = _per_dispatch(ins, attn_name, "SQ_INSTS_SALU")
-        waves, _ = _per_dispatch(ins, attn_name, "SQ_WAVES")
-        out["instructions_per_launch"] = {"SQ_INSTS_VALU": valu, "SQ_INSTS_MFMA": mfma, "SQ_INSTS_LDS": lds,
-                                          "SQ_INSTS_SALU": salu, "SQ_WAVES": waves,
-                                          "valu_per_mfma": valu / mfma if valu and mfma else None}
+        names = sorted({r["Counter_Name"] for r in ins})
+        per = {}
+        for c in names:
+            per[c], _ = _per_dispatch(ins, attn_name, c)
+        valu, mfma = per.get("SQ_INSTS_VALU"), per.get("SQ_INSTS_MFMA")
+        per["valu_per_mfma"] = valu / mfma if valu and mfma else None
+        out["instruction_counters_per_launch"] = per
+    # the gradient kernels, when the profiled run included the backward pass
+    bwd = {}
+    for kname in ("dkdv_kernel", "dq_kernel"):
+        b_busy, n_b = _per_dispatch(sq, kname, "SQ_VALU_MFMA_BUSY_CYCLES")
+        if not b_busy:
+            continue
+        b_gui, _ = _per_dispatch(sq, kname, "GRBM_GUI_ACTIVE", reduce="max")
+        b_mops, _ = _per_dispatch(sq, kname, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        bwd[kname] = {"mfma_busy_pct_of_gui_active": 100.0 * b_busy / (b_gui / 8 * SIMD_NUM) if b_gui else None,
+                      "mfma_bf16_flops_per_launch": b_mops * 512 if b_mops else None, "dispatches_averaged": n_b}
+    if bwd:
+        out["backward_kernels"] = bwd
     path = os.path.join(ROOT, "profiles", f"{attn_name}_{w.name}_hbm_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -585,12 +608,17 @@ _MASKS = {"0": "no mask", "1": "mask", "2": "strided mask"}
 def _kernel_label(name):
     import re
 
-    m = re.search(r"attention_bf16_kernel<(\d+), (\d), (\d)>", name)
+    m = re.search(r"attention_bf16_kernel<(\d+), (\d), (\d)(?:, (true|false))?>", name)
     if m:
-        return f"attention_bf16_kernel<{m.group(1)}, {_MODES[m.group(2)]}, {_MASKS[m.group(3)]}>"
-    m = re.search(r"attention_kernel<([\w_ ]+), (\d+), (\d)>", name)
+        sp = ", block-sparse" if m.group(4) == "true" else ""
+        return f"attention_bf16_kernel<{m.group(1)}, {_MODES[m.group(2)]}, {_MASKS[m.group(3)]}{sp}>"
+    m = re.search(r"attention_kernel<([\w_ ]+), (\d+), (\d)(?:, (true|false))?>", name)
     if m:
-        return f"attention_kernel<{m.group(1)}, {m.group(2)}, {_MODES[m.group(3)]}>"
+        sp = ", block-sparse" if m.group(4) == "true" else ""
+        return f"attention_kernel<{m.group(1)}, {m.group(2)}, {_MODES[m.group(3)]}{sp}>"
+    for k in ("sparse_bits_kernel", "sparse_plan_kernel"):
+        if k in name:
+            return k
     m = re.search(r"(dkdv_kernel|dq_kernel)<(\d+)>", name)
     if m:
         return f"{m.group(1)}<{m.group(2)}>"
@@ -636,16 +664,30 @@ def summarize_trace(args):
            "| Kernel | Calls | Average µs | Min µs | Max µs |", "|---|---|---|---|---|"]
     for lab, (calls, tot, mn, mx) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
         out.append(f"| {lab} | {calls} | {tot / calls / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} |")
-    out += ["", "Each share's attention kernel in the trace against the library's kernel timer in the same run "
-            "(the kernel variant of a share is unique to it in this run, so the trace's average is that share's "
-            "own; it includes the untimed settle and warm-up calls):", "",
+    out += ["", "Each share's attention kernel in the trace, averaged over the dispatches of its timed calls (taken "
+            "from kernel_trace.csv in launch order), against the library's kernel timer over the same calls:", "",
             "| Share | Kernel | Trace average µs | TFLOP/s (trace) | % of 2500 | Kernel timer µs | TFLOP/s (timer) |",
             "|---|---|---|---|---|---|---|"]
-    shares = [(head, d["roofline"]["kernel_ms"], d["config"]["counted_flops"])]
+    # dispatches of each kernel in launch order (kernel_trace.csv): a share's calls are the next
+    # (estimate calls + settle + warm-up + steps) dispatches of its kernel variant, shares in the order the
+    # benchmark runs them (the headline first, then the configs block)
+    traces = sorted(glob.glob(os.path.join(tdir, "**", "*kernel_trace.csv"), recursive=True))
+    disp = {}
+    if traces:
+        rows_t = list(csv.DictReader(open(traces[0])))
+        key = "Dispatch_Id" if "Dispatch_Id" in rows_t[0] else "Correlation_Id"
+        for r in sorted(rows_t, key=lambda r: int(r[key])):
+            lab = _kernel_label(r["Kernel_Name"])
+            if lab:
+                disp.setdefault(lab, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    shares = [(head, d["roofline"]["kernel_ms"], d["config"]["counted_flops"],
+               d["clock_settle"]["calls"] + d["warmup"] + d["steps"], d["steps"])]
     for name, e in d.get("configs", {}).items():
-        shares.append((name, e["kernel_ms"], e["counted_flops"]))
+        shares.append((name, e["kernel_ms"], e["counted_flops"], 2 + e["clock_settle_calls"] + e["warmup"] + e["steps"],
+                       e["steps"]))
     by_name = {wl.config(i).name: wl.config(i) for i in wl.CONFIGS}
-    for name, kms, flops in shares:
+    used = {}
+    for name, kms, flops, ncalls, nsteps in shares:
         w = by_name.get(name)
         if w is None:
             continue
@@ -654,10 +696,14 @@ def summarize_trace(args):
                                                                     else "0")
         dp = 32 if w.head_dim <= 32 else (64 if w.head_dim <= 64 else 128)
         lab = f"attention_bf16_kernel<{dp}, {_MODES[mode]}, {_MASKS[mask]}>"
-        if lab not in stats:
+        seq = disp.get(lab, [])
+        first = used.get(lab, 0)
+        mine = seq[first:first + ncalls]
+        used[lab] = first + ncalls
+        if not mine:
             continue
-        calls, tot, _, _ = stats[lab]
-        avg = tot / calls / 1e3
+        timed_calls = mine[-nsteps:]  # the timed calls are the last of the share's calls
+        avg = sum(timed_calls) / len(timed_calls)
         out.append(f"| {name} | {lab} | {avg:.1f} | {flops / (avg * 1e-6) / 1e12:.0f} | "
                    f"{100 * flops / (avg * 1e-6) / 1e12 / BF16_PEAK_TFLOPS:.1f} | {kms * 1e3:.1f} | "
                    f"{flops / (kms * 1e-3) / 1e12:.0f} |")
