@@ -18,8 +18,9 @@
 //  * dkdv_kernel: a workgroup owns 128 keys of one (batch, kv head), 32 per
 //    wave, and walks every query row of every query head of its group in
 //    blocks of 32. K and V stay in registers as MFMA B operands; each query
-//    block (Q, dO, lse, delta, positions) is staged once in LDS for the four
-//    waves, its global loads issued one block ahead. S = Q K^T and dP = dO V^T
+//    block (Q, dO, lse, delta, positions) is staged once in a ring of LDS
+//    slots for the four waves, its global loads issued two blocks ahead, and
+//    the work is software-pipelined across blocks (see the kernel). S = Q K^T and dP = dO V^T
 //    put one key per lane and 16 queries in its registers; those registers,
 //    rounded to bf16, are directly the B operand of dV^T += dO^T P and
 //    dK^T += Q^T dS, whose A operands are read transposed from the row-major
@@ -187,23 +188,61 @@ struct Tile {
 __device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // ---------------------------------------------------------------------------
-// dK and dV of 128 keys per workgroup.
+// dK and dV of 128 keys per workgroup, software-pipelined over query blocks.
+//
+// The query blocks the workgroup visits pass through a ring of four LDS slots
+// (Q, dO, lse, delta and positions of 32 rows each). Iteration i of the walk
+// first writes block i + 2, loaded into registers during the previous
+// iteration, into its slot and issues the global loads of block i + 3. Then
+// one phase of fixed slots: each slot issues one MFMA, alternately a product
+// of dV/dK for block i - 1 (from the bf16 P and dS the previous phase made)
+// and one of S/dP for block i + 1, and the vector units turn S(i) and dP(i),
+// finished in the previous phase, into the bf16 P(i) and dS(i) of the next
+// phase. No vector instruction of a phase waits on an MFMA of that phase, and
+// the matrix pipe always has independent work queued. One barrier closes the
+// iteration: it publishes block i + 2 and frees the slot of block i - 1.
+// Every accumulator sums its products in the same order as a plain loop over
+// the blocks would.
+
+template <int DP>
+struct QBlock {
+  __bf16 q[kRows * Tile<DP>::RS];
+  __bf16 g[kRows * Tile<DP>::RS];
+  float lse2[kRows];  // lse * log2(e) (0 for rows that see nothing)
+  float del[kRows];
+  int qp[kRows];
+};
+constexpr int kRing = 4;
+
+// Slot of a phase of nmf slots in which register r of S and dP is turned into P and dS.
+constexpr int vec_slot(int r, int nmf) {
+  int sl = 0;
+  while (16 * (sl + 1) / nmf <= r) ++sl;
+  return sl;
+}
+
+template <int V>
+struct BIntC {
+  static constexpr int value = V;
+};
+
+__device__ __forceinline__ bf16x8 words_bf16x8(const uint32_t (&w)[4]) {
+  return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
 
 // Two workgroups per CU where the registers allow (head_dim <= 64): the waves of
 // one then hide the barrier and LDS latency of the other.
 constexpr int dkdv_resident(int dp) { return dp <= 64 ? 2 : 1; }
 
-template <int DP>
+template <int DP, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(BwdParams p) {
   using T = Tile<DP>;
-  constexpr int NS = DP / 16;  // k-steps over head_dim
-  constexpr int NB = DP / 32;  // 32-row blocks of head_dim
+  constexpr int NS = DP / 16;           // k-steps over head_dim
+  constexpr int NB = DP / 32;           // 32-row blocks of head_dim
   constexpr int PER = T::PER;
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[kRows * T::RS];
-  __shared__ __attribute__((aligned(16))) __bf16 Gs[kRows * T::RS];
-  __shared__ __attribute__((aligned(16))) float lse2s[kRows];
-  __shared__ __attribute__((aligned(16))) float dels[kRows];
-  __shared__ __attribute__((aligned(16))) int qps[kRows];
+  constexpr int NMF = 4 * NB + 2 * NS;  // MFMAs per phase: dV/dK of one block and S/dP of another
+  constexpr int kRA = DP >= 128 ? 4 : 2;  // slots between an operand read and its MFMA
+  __shared__ __attribute__((aligned(16))) QBlock<DP> ring[kRing];
   __shared__ int kmin_red[2 * kBwdWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
@@ -261,7 +300,8 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
     dvT[i] = f32x16{};
   }
 
-  // walk (query head of the group, 32-row block) in order, skipping blocks that see none of our keys
+  // walk (query head of the group, 32-row block) in order, skipping blocks that see none of our keys;
+  // never called again once it has returned false
   const int n_qb = (int)((p.Lq + kRows - 1) / kRows);
   auto advance = [&](int& g, int& qb) {
     while (true) {
@@ -269,7 +309,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
         qb = 0;
         if (++g >= group) return false;
       }
-      if (!p.causal || p.qblk[2 * qb + 1] >= kmin) return true;
+      if (!CAUSAL || p.qblk[2 * qb + 1] >= kmin) return true;
     }
   };
   u32x4 pq[PER], pg[PER];
@@ -296,75 +336,167 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
       pp = v ? p.qpos[r0 + tid] : kPosMinQ;
     }
   };
-
-  int cg = 0, cqb = -1;
-  bool have = advance(cg, cqb);
-  if (have) fetch(cg, cqb);
-  while (have) {
-    __syncthreads();  // the previous block's LDS reads are done
-    T::put(Qs, tid, pq);
-    T::put(Gs, tid, pg);
+  auto put = [&](QBlock<DP>& s) {
+    T::put(s.q, tid, pq);
+    T::put(s.g, tid, pg);
     if (tid < kRows) {
-      lse2s[tid] = (pl == -INFINITY) ? 0.f : pl * kLog2e;
-      dels[tid] = pd;
-      qps[tid] = pp;
+      s.lse2[tid] = (pl == -INFINITY) ? 0.f : pl * kLog2e;
+      s.del[tid] = pd;
+      s.qp[tid] = pp;
+    }
+  };
+
+  // S and dP of one block, and the bf16 words of P and dS of two blocks (set = block parity; [t][w]
+  // holds registers 8t + 2w, 8t + 2w + 1)
+  f32x16 sc, dpc;
+  uint32_t pw[2][2][4], dw[2][2][4];
+
+  // One phase (block i in ring slot u). Its first 4 NB slots each issue one dV/dK product of block
+  // i - 1 (query half t = k / (2 NB), column block (k mod 2 NB) / 2, dV for even k) while the vector
+  // units turn S(i) and dP(i) into the bf16 words of set C; its last 2 NS slots issue S and dP of
+  // block i + 1 (k-step k / 2, S for even k) into the same registers, whose old values are then dead.
+  auto phase = [&](auto c_c, int u) {
+    constexpr int C = decltype(c_c)::value, N = C ^ 1;
+    constexpr int NA = 4 * NB;  // slots with vector work
+    const QBlock<DP>& cur = ring[u];
+    const QBlock<DP>& prv = ring[(u + kRing - 1) % kRing];
+    const QBlock<DP>& nxt = ring[(u + 1) % kRing];
+    // tables of block i: registers 4j .. 4j+3 hold queries 8j + 4h .. +3; group j is read kRA slots
+    // before the slot that first uses it
+    f32x4 ls[4], de[4];
+    i32x4 qq[4];
+    auto read_tables = [&](int jj) {
+      ls[jj] = *(const f32x4*)(cur.lse2 + 8 * jj + 4 * h);
+      de[jj] = *(const f32x4*)(cur.del + 8 * jj + 4 * h);
+      if (CAUSAL) qq[jj] = *(const i32x4*)(cur.qp + 8 * jj + 4 * h);
+    };
+    bf16x8 opa[NMF];
+    auto read_op = [&](int sl) {
+      if (sl < NA) {
+        opa[sl] = T::cols_frag((sl & 1) ? prv.q : prv.g, lane, (sl % (2 * NB)) >> 1, sl / (2 * NB));
+      } else {
+        const int k = sl - NA;
+        opa[sl] = T::rows_frag((k & 1) ? nxt.g : nxt.q, lane, k >> 1);
+      }
+    };
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      if (vec_slot(4 * jj, NA) - kRA <= 0) read_tables(jj);
+#pragma unroll
+    for (int sl = 0; sl < kRA; ++sl) read_op(sl);
+    float xp[16], xd[16];
+#pragma unroll
+    for (int sl = 0; sl < NMF; ++sl) {
+      if (sl + kRA < NMF) read_op(sl + kRA);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (vec_slot(4 * jj, NA) - kRA == sl && sl > 0) read_tables(jj);
+      if (sl < NA) {
+        const int t = sl / (2 * NB), db = (sl % (2 * NB)) >> 1;
+        if (sl & 1)
+          dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], words_bf16x8(dw[N][t]), dkT[db], 0, 0, 0);
+        else
+          dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], words_bf16x8(pw[N][t]), dvT[db], 0, 0, 0);
+        // vector work: registers [16 sl / NA, 16 (sl + 1) / NA) of S(i) and dP(i); a pair of registers
+        // becomes one word of P and one of dS once its second member is done
+#pragma unroll
+        for (int r = 16 * sl / NA; r < 16 * (sl + 1) / NA; ++r) {
+          const int jj = r >> 2, e = r & 3;
+          xp[r] = __builtin_amdgcn_exp2f(sc[r] * p.c2 - ls[jj][e]);
+          if (CAUSAL) xp[r] = (kp <= qq[jj][e]) ? xp[r] : 0.f;
+          xd[r] = xp[r] * (dpc[r] - de[jj][e]);
+          if (r & 1) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 a2 = {(__bf16)xp[r - 1], (__bf16)xp[r]};
+            const bf16x2 d2 = {(__bf16)xd[r - 1], (__bf16)xd[r]};
+            uint32_t& wa = pw[C][r >> 3][(r & 7) >> 1];
+            uint32_t& wd = dw[C][r >> 3][(r & 7) >> 1];
+            wa = __builtin_bit_cast(uint32_t, a2);
+            wd = __builtin_bit_cast(uint32_t, d2);
+            asm volatile("" : "+v"(wa), "+v"(wd));
+          }
+        }
+      } else {
+        const int k = sl - NA, st = k >> 1;
+        if (k & 1)
+          dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], vf[st], st == 0 ? f32x16{} : dpc, 0, 0, 0);
+        else
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], kf[st], st == 0 ? f32x16{} : sc, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // A slot that receives no block (the walk has ended) gets lse = +inf and positions that see no key, so
+  // a phase over it makes zero P and dS with or without the mask; its Q and dO hold zeros or an older
+  // block's rows, always finite.
+  auto put_none = [&](QBlock<DP>& s) {
+    if (tid < kRows) {
+      s.lse2[tid] = INFINITY;
+      s.del[tid] = 0.f;
+      s.qp[tid] = kPosMinQ;
+    }
+  };
+
+  // Phases run in pairs until one whose block does not exist: phase n adds dV/dK of the last block
+  // n - 1, and a phase past it adds zeros.
+  int cg = 0, cqb = -1;
+  if (advance(cg, cqb)) {
+    {
+      u32x4* z = (u32x4*)ring;
+      constexpr int N16 = (int)(sizeof(ring) / 16);
+      for (int k = tid; k < N16; k += kBwdThreads) z[k] = u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();
-    // every query of this block sees every key of the workgroup: no mask (rows past the last
-    // query are zero in LDS, with lse and delta 0, and contribute nothing either way)
-    const bool full = !p.causal || p.qblk[2 * cqb] >= kmax;
-    have = advance(cg, cqb);
-    if (have) fetch(cg, cqb);  // in flight during the matrix work below
-
-    // S = Q K^T and dP = dO V^T: lane holds key lane % 32 and queries out_row(r)
-    f32x16 s = f32x16{}, dp = f32x16{};
+    fetch(cg, cqb);
+    put(ring[0]);
+    bool ok0 = true, ok1 = advance(cg, cqb), ok2 = false;
+    if (ok1) {
+      fetch(cg, cqb);
+      put(ring[1]);
+      ok2 = advance(cg, cqb);
+    } else {
+      put_none(ring[1]);
+    }
+    if (ok2) fetch(cg, cqb);  // written to its slot by the first iteration
+    __syncthreads();
+    sc = f32x16{};
+    dpc = f32x16{};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Qs, lane, st), kf[st], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Gs, lane, st), vf[st], dp, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(ring[0].q, lane, st), kf[st], sc, 0, 0, 0);
+      dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(ring[0].g, lane, st), vf[st], dpc, 0, 0, 0);
     }
-    // registers 4i .. 4i+3 hold queries 8i + 4h .. +3: one 16-byte LDS read per table and group
-    if (full) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q0 = 8 * i + 4 * h;
-        const f32x4 ls = *(const f32x4*)(lse2s + q0);
-        const f32x4 de = *(const f32x4*)(dels + q0);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * i + e;
-          const float pr = __builtin_amdgcn_exp2f(s[r] * p.c2 - ls[e]);
-          s[r] = pr;
-          dp[r] = pr * (dp[r] - de[e]);
-        }
+      for (int w = 0; w < 4; ++w) pw[1][t][w] = dw[1][t][w] = 0u;
+
+    int u = 0;  // ring slot of block i
+    auto step = [&](auto c_c) {
+      if (ok2)
+        put(ring[(u + 2) % kRing]);
+      else
+        put_none(ring[(u + 2) % kRing]);
+      bool ok3 = false;
+      if (ok2 && advance(cg, cqb)) {
+        ok3 = true;
+        fetch(cg, cqb);  // in flight during the phase
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q0 = 8 * i + 4 * h;
-        const f32x4 ls = *(const f32x4*)(lse2s + q0);
-        const f32x4 de = *(const f32x4*)(dels + q0);
-        const i32x4 qq = *(const i32x4*)(qps + q0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * i + e;
-          const float pr = (kp <= qq[e]) ? __builtin_amdgcn_exp2f(s[r] * p.c2 - ls[e]) : 0.f;
-          s[r] = pr;
-          dp[r] = pr * (dp[r] - de[e]);
-        }
-      }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (scale applied at the end)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 pf = to_bf16x8(s, t);
-      const bf16x8 df = to_bf16x8(dp, t);
-#pragma unroll
-      for (int db = 0; db < NB; ++db) {
-        dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(Gs, lane, db, t), pf, dvT[db], 0, 0, 0);
-        dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(Qs, lane, db, t), df, dkT[db], 0, 0, 0);
-      }
-    }
+      phase(c_c, u);
+      __syncthreads();
+      u = (u + 1) % kRing;
+      const bool real = ok0;
+      ok0 = ok1;
+      ok1 = ok2;
+      ok2 = ok3;
+      return real;
+    };
+    bool more;
+    do {
+      step(BIntC<0>{});
+      more = step(BIntC<1>{});
+    } while (more);
   }
 
   // lane writes its key's row: block db, registers 4i .. 4i+3 are columns db*32 + 8i + 4h .. +3
@@ -665,8 +797,13 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   const int64_t n_kt = (p.Lk + kGroupRows - 1) / kGroupRows;
   const int64_t n_qt = (p.Lq + kGroupRows - 1) / kGroupRows;
   timer_begin(s);
-  if (n_kt > 0)
-    hipLaunchKernelGGL((dkdv_kernel<DP>), dim3((unsigned)(n_kt * p.B * p.Hkv)), dim3(kBwdThreads), 0, s, p);
+  if (n_kt > 0) {
+    const dim3 grid((unsigned)(n_kt * p.B * p.Hkv));
+    if (p.causal)
+      hipLaunchKernelGGL((dkdv_kernel<DP, true>), grid, dim3(kBwdThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<DP, false>), grid, dim3(kBwdThreads), 0, s, p);
+  }
   timer_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
