@@ -94,6 +94,26 @@ struct BwdParams {
   float* dq_part;  // [dq_split][B * Hq * Lq][d] unscaled partial dQ when dq_split > 1 (workspace)
 };
 
+// Chunk descriptors read through the constant address space: with an index that is the same for every
+// lane these become scalar loads.
+typedef const __attribute__((address_space(4))) BwdChunk* cchunk_ptr;
+__device__ __forceinline__ BwdChunk chunk_at(const BwdChunk* chunks, int i) {
+  const cchunk_ptr c = (cchunk_ptr)chunks + i;
+  BwdChunk r;
+  r.k = c->k;
+  r.v = c->v;
+  r.start = c->start;
+  r.len = c->len;
+  r.sb = c->sb;
+  r.sh = c->sh;
+  r.ss = c->ss;
+  r.pos0 = c->pos0;
+  r.ps = c->ps;
+  return r;
+}
+typedef const __attribute__((address_space(4))) int* cint_ptr;
+__device__ __forceinline__ int cload(const int* p) { return *(cint_ptr)p; }
+
 // Row address of key j (chunk `c` holds it); the cursor only moves forward.
 __device__ __forceinline__ int64_t key_offset(const BwdParams& p, int64_t j, int b, int hk, int& c) {
   while (c + 1 < p.n_chunks && j >= p.chunks[c].start + p.chunks[c].len) ++c;
@@ -134,18 +154,29 @@ __global__ __launch_bounds__(256) void delta_kernel(int64_t rows, int d, int lpr
 }
 
 // ---------------------------------------------------------------------------
-// 32-row blocks of a [rows, d] bf16 tensor in LDS, row-major with a row stride
-// of DP + 16 elements: a transposing read then touches 16 distinct bank pairs
-// per 16 lanes. Blocks go HBM -> registers (issued one block ahead, so the
-// loads run under the current block's matrix work) -> LDS.
+// 32-row blocks of a [rows, d] bf16 tensor in LDS, row-major without padding,
+// the 16-byte pieces of each row permuted by an XOR swizzle (piece c of row r
+// sits at position c ^ swz(r)) so that both operand reads hit distinct banks:
+// 16 consecutive rows at one piece (row reads) and 4 consecutive rows x 4
+// consecutive pieces (transposing reads). Blocks go HBM -> registers (issued
+// ahead, so the loads run under earlier matrix work) -> LDS.
 
 template <int DP>
 struct Tile {
-  static constexpr int RS = DP + 16;                     // row stride (elements)
+  static constexpr int RS = DP;                          // row stride (elements)
+  static constexpr int ROWB = 2 * DP;                    // row stride (bytes)
+  static constexpr int NS = DP / 16;                     // k-steps over head_dim
+  static constexpr int NB = DP / 32;                     // 32-column blocks
   static constexpr int PIECES = kRows * DP / 8;          // 16-byte pieces per block
   static constexpr int PER = (PIECES + kBwdThreads - 1) / kBwdThreads;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (DP == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else if constexpr (DP == 64) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+  }
 
   // piece k of this thread: row and 8-column group; false past the block
   static __device__ __forceinline__ bool piece(int tid, int k, int& r, int& c8) {
@@ -159,27 +190,46 @@ struct Tile {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       int r, c8;
-      if (piece(tid, k, r, c8)) *(u32x4*)(rm + r * RS + c8 * 8) = regs[k];
+      if (piece(tid, k, r, c8)) *(u32x4*)(rm + r * RS + ((c8 ^ swz(r)) << 3)) = regs[k];
     }
   }
 
-  // A operand of a 32x32x16 MFMA: row lane % 32 of the block, k = 16 s + 8 h .. +7.
-  static __device__ __forceinline__ bf16x8 rows_frag(const __bf16* rm, int lane, int s) {
-    return *(const bf16x8*)(rm + (lane & 31) * RS + 16 * s + 8 * (lane >> 5));
+  // Per-lane LDS byte offsets of the operands, fixed for the whole kernel.
+  //  row[s]: A operand of a 32x32x16 MFMA, row lane % 32 of the block, k = 16 s + 8 h .. +7.
+  //  col[db][hh]: half hh of the A operand holding the block transposed: row db * 32 + lane % 32 of
+  //  the transpose (a column of the block), and k slots in the order of an MFMA output's registers
+  //  8t .. 8t+7, i.e. block rows 16t + 4h .. +3 (hh = 0), then 16t + 8 + 4h .. +3 (hh = 1); add 16t
+  //  rows, which leave the swizzle unchanged. Each half is one ds_read_b64_tr_b16: lane j of a 16-lane
+  //  group addresses block row base + j / 4, columns c0 + 4 (j % 4) .. +3, and lane i of the group
+  //  receives column c0 + i of block rows base .. base + 3.
+  struct Lanes {
+    int row[NS];
+    int col[NB][2];
+  };
+  static __device__ __forceinline__ Lanes lanes(int lane) {
+    Lanes L;
+    const int r = lane & 31, h = lane >> 5, j = lane & 15;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) L.row[s] = r * ROWB + (((2 * s + h) ^ swz(r)) << 4);
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 4 * h + 8 * hh + (j >> 2);
+        const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+        L.col[db][hh] = row * ROWB + (((col >> 3) ^ swz(row)) << 4) + 2 * (col & 7);
+      }
+    return L;
   }
 
-  // A operand holding the block transposed: row db * 32 + lane % 32 of the transpose (a column of
-  // the block), and k slots in the order of an MFMA output's registers 8t .. 8t+7, i.e. block rows
-  // 16t + 4h .. +3, then 16t + 8 + 4h .. +3. Each half is one ds_read_b64_tr_b16: lane j of a
-  // 16-lane group addresses block row base + j / 4, columns c0 + 4 (j % 4) .. +3, and lane i of the
-  // group receives column c0 + i of block rows base .. base + 3.
-  static __device__ __forceinline__ bf16x8 cols_frag(const __bf16* rm, int lane, int db, int t) {
-    const int j = lane & 15;
-    const int base = 16 * t + 4 * (lane >> 5) + (j >> 2);
-    const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-    const __bf16* a = rm + base * RS + col;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)a);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a + 8 * RS));
+  static __device__ __forceinline__ bf16x8 rows_frag(const __bf16* rm, const Lanes& L, int s) {
+    return *(const bf16x8*)((const char*)rm + L.row[s]);
+  }
+
+  static __device__ __forceinline__ bf16x8 cols_frag(const __bf16* rm, const Lanes& L, int db, int t) {
+    const char* a = (const char*)rm + t * 16 * ROWB;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a + L.col[db][0]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(a + L.col[db][1]));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
@@ -246,6 +296,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
   __shared__ int kmin_red[2 * kBwdWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const typename T::Lanes LL = T::lanes(lane);
   const int n_kt = (int)((p.Lk + kGroupRows - 1) / kGroupRows);
   const int kt = blockIdx.x % n_kt;
   const int bh = blockIdx.x / n_kt;
@@ -309,7 +360,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
         qb = 0;
         if (++g >= group) return false;
       }
-      if (!CAUSAL || p.qblk[2 * qb + 1] >= kmin) return true;
+      if (!CAUSAL || cload(p.qblk + 2 * qb + 1) >= kmin) return true;
     }
   };
   u32x4 pq[PER], pg[PER];
@@ -373,10 +424,10 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
     bf16x8 opa[NMF];
     auto read_op = [&](int sl) {
       if (sl < NA) {
-        opa[sl] = T::cols_frag((sl & 1) ? prv.q : prv.g, lane, (sl % (2 * NB)) >> 1, sl / (2 * NB));
+        opa[sl] = T::cols_frag((sl & 1) ? prv.q : prv.g, LL, (sl % (2 * NB)) >> 1, sl / (2 * NB));
       } else {
         const int k = sl - NA;
-        opa[sl] = T::rows_frag((k & 1) ? nxt.g : nxt.q, lane, k >> 1);
+        opa[sl] = T::rows_frag((k & 1) ? nxt.g : nxt.q, LL, k >> 1);
       }
     };
 #pragma unroll
@@ -397,14 +448,21 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
           dkT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], words_bf16x8(dw[N][t]), dkT[db], 0, 0, 0);
         else
           dvT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], words_bf16x8(pw[N][t]), dvT[db], 0, 0, 0);
-        // vector work: registers [16 sl / NA, 16 (sl + 1) / NA) of S(i) and dP(i); a pair of registers
-        // becomes one word of P and one of dS once its second member is done
+      } else {
+        const int k = sl - NA, st = k >> 1;
+        if (k & 1)
+          dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], vf[st], st == 0 ? f32x16{} : dpc, 0, 0, 0);
+        else
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], kf[st], st == 0 ? f32x16{} : sc, 0, 0, 0);
+      }
+      // Vector work on registers [16 s / NA, 16 (s + 1) / NA) of S(i) and dP(i), in two stages so that
+      // a slot's instructions do not wait on each other: P in slot s, then dS and the bf16 words of each
+      // finished pair in slot s + 1 (the last of these runs in the first S/dP slot, before dP is
+      // overwritten one slot later).
+      if (sl >= 1 && sl - 1 < NA) {
 #pragma unroll
-        for (int r = 16 * sl / NA; r < 16 * (sl + 1) / NA; ++r) {
-          const int jj = r >> 2, e = r & 3;
-          xp[r] = __builtin_amdgcn_exp2f(sc[r] * p.c2 - ls[jj][e]);
-          if (CAUSAL) xp[r] = (kp <= qq[jj][e]) ? xp[r] : 0.f;
-          xd[r] = xp[r] * (dpc[r] - de[jj][e]);
+        for (int r = 16 * (sl - 1) / NA; r < 16 * sl / NA; ++r) {
+          xd[r] = xp[r] * (dpc[r] - de[r >> 2][r & 3]);
           if (r & 1) {
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             const bf16x2 a2 = {(__bf16)xp[r - 1], (__bf16)xp[r]};
@@ -416,12 +474,14 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
             asm volatile("" : "+v"(wa), "+v"(wd));
           }
         }
-      } else {
-        const int k = sl - NA, st = k >> 1;
-        if (k & 1)
-          dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], vf[st], st == 0 ? f32x16{} : dpc, 0, 0, 0);
-        else
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], kf[st], st == 0 ? f32x16{} : sc, 0, 0, 0);
+      }
+      if (sl < NA) {
+#pragma unroll
+        for (int r = 16 * sl / NA; r < 16 * (sl + 1) / NA; ++r) {
+          const int jj = r >> 2, e = r & 3;
+          xp[r] = __builtin_amdgcn_exp2f(sc[r] * p.c2 - ls[jj][e]);
+          if (CAUSAL) xp[r] = (kp <= qq[jj][e]) ? xp[r] : 0.f;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -464,8 +524,8 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
     dpc = f32x16{};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(ring[0].q, lane, st), kf[st], sc, 0, 0, 0);
-      dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(ring[0].g, lane, st), vf[st], dpc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(ring[0].q, LL, st), kf[st], sc, 0, 0, 0);
+      dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(ring[0].g, LL, st), vf[st], dpc, 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -520,7 +580,20 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
 }
 
 // ---------------------------------------------------------------------------
-// dQ of 128 query rows per workgroup.
+// dQ of 128 query rows per workgroup, software-pipelined over key tiles in the
+// same way as dK/dV: key tiles pass through a ring of four LDS slots (K, V and
+// key positions of 32 keys); phase i issues the dQ products of tile i - 1
+// while the vector units turn S(i), dP(i) into the bf16 dS of set i mod 2, then
+// S/dP of tile i + 1; one barrier per tile. Every score is masked by position
+// (keys past the end and tiles past the walk have position "after
+// everything"), which also keeps exp(-lse) of a missing key out of the sums.
+
+template <int DP>
+struct KTile {
+  __bf16 k[kRows * Tile<DP>::RS];
+  __bf16 v[kRows * Tile<DP>::RS];
+  int kp[kRows];
+};
 
 template <int DP>
 __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
@@ -528,12 +601,14 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   constexpr int NS = DP / 16;
   constexpr int NB = DP / 32;
   constexpr int PER = T::PER;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kRows * T::RS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[kRows * T::RS];
-  __shared__ __attribute__((aligned(16))) int kps[kRows];
+  constexpr int NA = 2 * NB;            // dQ products per phase (slots with vector work)
+  constexpr int NMF = NA + 2 * NS;      // MFMAs per phase
+  constexpr int kRA = 2;                // slots between an operand read and its MFMA
+  __shared__ __attribute__((aligned(16))) KTile<DP> ring[kRing];
   __shared__ int qmax_red[2 * kBwdWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const typename T::Lanes LL = T::lanes(lane);
   const int n_qt = (int)((p.Lq + kGroupRows - 1) / kGroupRows);
   const int qt = blockIdx.x % n_qt;
   const int rest = blockIdx.x / n_qt;
@@ -561,38 +636,33 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   const float lse2 = (lsev == -INFINITY) ? 0.f : lsev * kLog2e;
   const float del = qvalid ? p.delta[row] : 0.f;
   const int qp = qvalid ? p.qpos[i] : kPosMinQ;
-  int wq = qp, wn = qvalid ? qp : kPosMax;
-  for (int o = 32; o > 0; o >>= 1) {
-    wq = max(wq, __shfl_xor(wq, o));
-    wn = min(wn, __shfl_xor(wn, o));
-  }
-  if (lane == 0) {
-    qmax_red[wave] = wq;
-    qmax_red[kBwdWaves + wave] = wn;
-  }
+  int wq = qp;
+  for (int o = 32; o > 0; o >>= 1) wq = max(wq, __shfl_xor(wq, o));
+  if (lane == 0) qmax_red[wave] = wq;
   __syncthreads();
-  int qmax = qmax_red[0], qmin = qmax_red[kBwdWaves];
-  for (int w = 1; w < kBwdWaves; ++w) {
-    qmax = max(qmax, qmax_red[w]);
-    qmin = min(qmin, qmax_red[kBwdWaves + w]);
-  }
+  int qmax = qmax_red[0];
+  for (int w = 1; w < kBwdWaves; ++w) qmax = max(qmax, qmax_red[w]);
 
   f32x16 dqT[NB];
 #pragma unroll
   for (int db = 0; db < NB; ++db) dqT[db] = f32x16{};
 
   // key tiles of 32 in list order (this workgroup's range of them when the key range is split),
-  // skipping tiles after every query of the workgroup
+  // skipping tiles after every query of the workgroup; never called again once it has returned false
   const int n_kt_all = (int)((p.Lk + kRows - 1) / kRows);
   const int per_split = (n_kt_all + p.dq_split - 1) / p.dq_split;
   const int t_beg = split * per_split;
   const int n_kt = min(n_kt_all, t_beg + per_split);
   auto advance = [&](int& t) {
     while (++t < n_kt)
-      if (!p.causal || p.ktile[2 * t] <= qmax) return true;
+      if (!p.causal || cload(p.ktile + 2 * t) <= qmax) return true;
     return false;
   };
-  // staging cursors: each thread's pieces keep their row slot from tile to tile
+  // The chunk that holds a tile's first key is tracked by a cursor that is the same for every lane
+  // (its descriptor reads are scalar and cached); a tile inside that chunk takes its row addresses
+  // from it directly, and only a tile that crosses a chunk end looks up each row's chunk (per-piece
+  // cursors that only move forward).
+  int cc = 0;
   int cur[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) cur[k] = 0;
@@ -600,72 +670,174 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   int pkp = kPosMax;
   auto fetch = [&](int t) {
     const int64_t j0 = (int64_t)t * kRows;
+    const cchunk_ptr chunks = (cchunk_ptr)p.chunks;
+    while (cc + 1 < p.n_chunks && j0 >= chunks[cc].start + chunks[cc].len) ++cc;
+    const BwdChunk ch = chunk_at(p.chunks, cc);
+    const bool inside = j0 + kRows <= ch.start + ch.len;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       int r, c8;
       pk[k] = u32x4{0u, 0u, 0u, 0u};
       pv[k] = u32x4{0u, 0u, 0u, 0u};
       if (T::piece(tid, k, r, c8) && j0 + r < p.Lk && c8 * 8 < p.d) {
-        const int64_t off = key_offset(p, j0 + r, b, hk, cur[k]);
-        pk[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].k + off + c8 * 8);
-        pv[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].v + off + c8 * 8);
+        if (inside) {
+          const int64_t off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j0 + r - ch.start) * ch.ss + c8 * 8;
+          pk[k] = *(const u32x4*)((const __bf16*)ch.k + off);
+          pv[k] = *(const u32x4*)((const __bf16*)ch.v + off);
+        } else {
+          cur[k] = max(cur[k], cc);
+          const int64_t off = key_offset(p, j0 + r, b, hk, cur[k]);
+          pk[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].k + off + c8 * 8);
+          pv[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].v + off + c8 * 8);
+        }
       }
     }
     if (tid < kRows) pkp = (j0 + tid < p.Lk) ? p.kpos[j0 + tid] : kPosMax;
   };
+  auto put = [&](KTile<DP>& s) {
+    T::put(s.k, tid, pk);
+    T::put(s.v, tid, pv);
+    if (tid < kRows) s.kp[tid] = pkp;
+  };
+  // a slot that receives no tile: keys after everything, so its scores are all masked
+  auto put_none = [&](KTile<DP>& s) {
+    if (tid < kRows) s.kp[tid] = kPosMax;
+  };
 
-  int t = t_beg - 1;
-  bool have = advance(t);
-  if (have) fetch(t);
-  while (have) {
-    __syncthreads();
-    T::put(Ks, tid, pk);
-    T::put(Vs, tid, pv);
-    if (tid < kRows) kps[tid] = pkp;
-    __syncthreads();
-    // every key of this (complete) tile is seen by every query of the workgroup: no mask. The
-    // last tile keeps it: its missing keys have zero rows, but exp(-lse) of such a key could
-    // overflow and turn 0 * inf into NaN
-    const bool full = (int64_t)(t + 1) * kRows <= p.Lk && (!p.causal || p.ktile[2 * t + 1] <= qmin);
-    have = advance(t);
-    if (have) fetch(t);  // in flight during the matrix work below
+  // S^T and dP^T of one tile (lane: query lane % 32, registers: keys out_row(r)), and the bf16 words of
+  // dS of two tiles (set = tile parity; [t][w] holds registers 8t + 2w, 8t + 2w + 1)
+  f32x16 sc, dpc;
+  uint32_t dw[2][2][4];
 
-    // S^T = K Q^T and dP^T = V dO^T: lane holds query lane % 32 and keys out_row(r)
-    f32x16 s = f32x16{}, dp = f32x16{};
+  // One phase (tile i in ring slot u): NA slots of dQ products of tile i - 1 (key half t = k / NB,
+  // column block k mod NB) with the vector work on S(i), dP(i), then 2 NS slots of S and dP of tile
+  // i + 1 (k-step k / 2, S for even k) into the same registers.
+  auto phase = [&](auto c_c, int u) {
+    constexpr int C = decltype(c_c)::value, N = C ^ 1;
+    const KTile<DP>& cur_t = ring[u];
+    const KTile<DP>& prv = ring[(u + kRing - 1) % kRing];
+    const KTile<DP>& nxt = ring[(u + 1) % kRing];
+    i32x4 kk[4];  // key positions of registers 4j .. 4j+3: keys 8j + 4h .. +3
+    auto read_keys = [&](int jj) { kk[jj] = *(const i32x4*)(cur_t.kp + 8 * jj + 4 * h); };
+    bf16x8 opa[NMF];
+    auto read_op = [&](int sl) {
+      if (sl < NA) {
+        opa[sl] = T::cols_frag(prv.k, LL, sl % NB, sl / NB);
+      } else {
+        const int k = sl - NA;
+        opa[sl] = T::rows_frag((k & 1) ? nxt.v : nxt.k, LL, k >> 1);
+      }
+    };
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Ks, lane, st), qf[st], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(Vs, lane, st), gf[st], dp, 0, 0, 0);
-    }
-    if (full) {
+    for (int jj = 0; jj < 4; ++jj)
+      if (vec_slot(4 * jj, NA) - kRA <= 0) read_keys(jj);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2) * (dp[r] - del);
-    } else {
+    for (int sl = 0; sl < kRA; ++sl) read_op(sl);
+    float xp[16], xd[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const i32x4 kk = *(const i32x4*)(kps + 8 * i + 4 * h);  // keys of registers 4i .. 4i+3
+    for (int sl = 0; sl < NMF; ++sl) {
+      if (sl + kRA < NMF) read_op(sl + kRA);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * i + e;
-          const float pr = (kk[e] <= qp) ? __builtin_amdgcn_exp2f(s[r] * p.c2 - lse2) : 0.f;
-          dp[r] = pr * (dp[r] - del);
+      for (int jj = 0; jj < 4; ++jj)
+        if (vec_slot(4 * jj, NA) - kRA == sl && sl > 0) read_keys(jj);
+      if (sl < NA) {
+        const int tt = sl / NB, db = sl % NB;
+        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], words_bf16x8(dw[N][tt]), dqT[db], 0, 0, 0);
+      } else {
+        const int k = sl - NA, st = k >> 1;
+        if (k & 1)
+          dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], gf[st], st == 0 ? f32x16{} : dpc, 0, 0, 0);
+        else
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[sl], qf[st], st == 0 ? f32x16{} : sc, 0, 0, 0);
+      }
+      // vector work in two stages as in the dK/dV kernel: P in slot s, dS and its words in slot s + 1
+      if (sl >= 1 && sl - 1 < NA) {
+#pragma unroll
+        for (int r = 16 * (sl - 1) / NA; r < 16 * sl / NA; ++r) {
+          xd[r] = xp[r] * (dpc[r] - del);
+          if (r & 1) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 d2 = {(__bf16)xd[r - 1], (__bf16)xd[r]};
+            uint32_t& wd = dw[C][r >> 3][(r & 7) >> 1];
+            wd = __builtin_bit_cast(uint32_t, d2);
+            asm volatile("" : "+v"(wd));
+          }
         }
       }
-    }
-    // dQ^T += K^T dS^T (scale applied at the end)
+      if (sl < NA) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const bf16x8 df = to_bf16x8(dp, tt);
-#pragma unroll
-      for (int db = 0; db < NB; ++db)
-        dqT[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::cols_frag(Ks, lane, db, tt), df, dqT[db], 0, 0, 0);
+        for (int r = 16 * sl / NA; r < 16 * (sl + 1) / NA; ++r)
+          xp[r] = (kk[r >> 2][r & 3] <= qp) ? __builtin_amdgcn_exp2f(sc[r] * p.c2 - lse2) : 0.f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // Phases run in pairs until one whose tile does not exist: phase n adds dQ of the last tile n - 1,
+  // and a phase past it adds zeros.
+  int t = t_beg - 1;
+  if (advance(t)) {
+    {
+      u32x4* z = (u32x4*)ring;
+      constexpr int N16 = (int)(sizeof(ring) / 16);
+      for (int k = tid; k < N16; k += kBwdThreads) z[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    fetch(t);
+    put(ring[0]);
+    bool ok0 = true, ok1 = advance(t), ok2 = false;
+    if (ok1) {
+      fetch(t);
+      put(ring[1]);
+      ok2 = advance(t);
+    } else {
+      put_none(ring[1]);
+    }
+    if (ok2) fetch(t);  // written to its slot by the first iteration
+    __syncthreads();
+    sc = f32x16{};
+    dpc = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(ring[0].k, LL, st), qf[st], sc, 0, 0, 0);
+      dpc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::rows_frag(ring[0].v, LL, st), gf[st], dpc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) dw[1][tt][w] = 0u;
+
+    int u = 0;  // ring slot of tile i
+    auto step = [&](auto c_c) {
+      if (ok2)
+        put(ring[(u + 2) % kRing]);
+      else
+        put_none(ring[(u + 2) % kRing]);
+      bool ok3 = false;
+      if (ok2 && advance(t)) {
+        ok3 = true;
+        fetch(t);  // in flight during the phase
+      }
+      phase(c_c, u);
+      __syncthreads();
+      u = (u + 1) % kRing;
+      const bool real = ok0;
+      ok0 = ok1;
+      ok1 = ok2;
+      ok2 = ok3;
+      return real;
+    };
+    bool more;
+    do {
+      step(BIntC<0>{});
+      more = step(BIntC<1>{});
+    } while (more);
   }
 
   if (qvalid) {
     // one range: dQ itself; several: this range's unscaled partial, summed by dq_reduce_kernel
     const bool direct = p.dq_split == 1;
-    const float sc = direct ? p.scale : 1.f;
+    const float sc_out = direct ? p.scale : 1.f;
     float* dqr = direct ? p.dq + row * p.d
                         : p.dq_part + ((int64_t)split * p.B * p.Hq * p.Lq + row) * p.d;
 #pragma unroll
@@ -674,8 +846,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
       for (int k = 0; k < 4; ++k) {
         const int col = db * 32 + 8 * k + 4 * h;
         if (col < p.d) {
-          const f32x4 v = {dqT[db][4 * k] * sc, dqT[db][4 * k + 1] * sc, dqT[db][4 * k + 2] * sc,
-                           dqT[db][4 * k + 3] * sc};
+          const f32x4 v = {dqT[db][4 * k] * sc_out, dqT[db][4 * k + 1] * sc_out, dqT[db][4 * k + 2] * sc_out,
+                           dqT[db][4 * k + 3] * sc_out};
           *(f32x4*)(dqr + col) = v;
         }
       }
