@@ -584,9 +584,13 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
 // same way as dK/dV: key tiles pass through a ring of four LDS slots (K, V and
 // key positions of 32 keys); phase i issues the dQ products of tile i - 1
 // while the vector units turn S(i), dP(i) into the bf16 dS of set i mod 2, then
-// S/dP of tile i + 1; one barrier per tile. Every score is masked by position
-// (keys past the end and tiles past the walk have position "after
-// everything"), which also keeps exp(-lse) of a missing key out of the sums.
+// S/dP of tile i + 1; one barrier per tile. With the causal mask every score
+// is masked by position (keys past the end and tiles past the walk have
+// position "after everything"). Without it no score is masked: the exponent
+// is clamped at 0 (lse is at least every score, so this only absorbs
+// rounding), which keeps exp(-lse) of a missing key, whose K and V rows are
+// zero, finite, and tiles past the walk get zero K rows, so their products
+// add nothing.
 
 template <int DP>
 struct KTile {
@@ -595,7 +599,7 @@ struct KTile {
   int kp[kRows];
 };
 
-template <int DP>
+template <int DP, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   using T = Tile<DP>;
   constexpr int NS = DP / 16;
@@ -655,7 +659,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   const int n_kt = min(n_kt_all, t_beg + per_split);
   auto advance = [&](int& t) {
     while (++t < n_kt)
-      if (!p.causal || cload(p.ktile + 2 * t) <= qmax) return true;
+      if (!CAUSAL || cload(p.ktile + 2 * t) <= qmax) return true;
     return false;
   };
   // The chunk that holds a tile's first key is tracked by a cursor that is the same for every lane
@@ -673,7 +677,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
     const cchunk_ptr chunks = (cchunk_ptr)p.chunks;
     while (cc + 1 < p.n_chunks && j0 >= chunks[cc].start + chunks[cc].len) ++cc;
     const BwdChunk ch = chunk_at(p.chunks, cc);
-    const bool inside = j0 + kRows <= ch.start + ch.len;
+    // the whole tile in one chunk whose 32 rows span less than 2 GB: a base address shared by all
+    // lanes plus 32-bit lane offsets
+    const bool inside = j0 + kRows <= ch.start + ch.len && ch.ss <= (0x7fffffff / (2 * kRows));
+    const int64_t tile_off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j0 - ch.start) * ch.ss;
+    const char* kbase = (const char*)((const __bf16*)ch.k + tile_off);
+    const char* vbase = (const char*)((const __bf16*)ch.v + tile_off);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       int r, c8;
@@ -681,9 +690,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
       pv[k] = u32x4{0u, 0u, 0u, 0u};
       if (T::piece(tid, k, r, c8) && j0 + r < p.Lk && c8 * 8 < p.d) {
         if (inside) {
-          const int64_t off = (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j0 + r - ch.start) * ch.ss + c8 * 8;
-          pk[k] = *(const u32x4*)((const __bf16*)ch.k + off);
-          pv[k] = *(const u32x4*)((const __bf16*)ch.v + off);
+          const uint32_t off = (uint32_t)r * (uint32_t)(2 * ch.ss) + (uint32_t)(c8 * 16);
+          pk[k] = *(const u32x4*)(kbase + off);
+          pv[k] = *(const u32x4*)(vbase + off);
         } else {
           cur[k] = max(cur[k], cc);
           const int64_t off = key_offset(p, j0 + r, b, hk, cur[k]);
@@ -692,16 +701,25 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
         }
       }
     }
-    if (tid < kRows) pkp = (j0 + tid < p.Lk) ? p.kpos[j0 + tid] : kPosMax;
+    if (CAUSAL && tid < kRows) pkp = (j0 + tid < p.Lk) ? p.kpos[j0 + tid] : kPosMax;
   };
   auto put = [&](KTile<DP>& s) {
     T::put(s.k, tid, pk);
     T::put(s.v, tid, pv);
-    if (tid < kRows) s.kp[tid] = pkp;
+    if (CAUSAL && tid < kRows) s.kp[tid] = pkp;
   };
-  // a slot that receives no tile: keys after everything, so its scores are all masked
+  // a slot that receives no tile: keys after everything (causal), or zero K rows (not causal), so the
+  // products of its tile add nothing
   auto put_none = [&](KTile<DP>& s) {
-    if (tid < kRows) s.kp[tid] = kPosMax;
+    if constexpr (CAUSAL) {
+      if (tid < kRows) s.kp[tid] = kPosMax;
+    } else {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      u32x4 zr[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) zr[k] = z;
+      T::put(s.k, tid, zr);
+    }
   };
 
   // S^T and dP^T of one tile (lane: query lane % 32, registers: keys out_row(r)), and the bf16 words of
@@ -718,7 +736,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
     const KTile<DP>& prv = ring[(u + kRing - 1) % kRing];
     const KTile<DP>& nxt = ring[(u + 1) % kRing];
     i32x4 kk[4];  // key positions of registers 4j .. 4j+3: keys 8j + 4h .. +3
-    auto read_keys = [&](int jj) { kk[jj] = *(const i32x4*)(cur_t.kp + 8 * jj + 4 * h); };
+    auto read_keys = [&](int jj) {
+      if (CAUSAL) kk[jj] = *(const i32x4*)(cur_t.kp + 8 * jj + 4 * h);
+    };
     bf16x8 opa[NMF];
     auto read_op = [&](int sl) {
       if (sl < NA) {
@@ -767,7 +787,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
       if (sl < NA) {
 #pragma unroll
         for (int r = 16 * sl / NA; r < 16 * (sl + 1) / NA; ++r)
-          xp[r] = (kk[r >> 2][r & 3] <= qp) ? __builtin_amdgcn_exp2f(sc[r] * p.c2 - lse2) : 0.f;
+          if (CAUSAL)
+            xp[r] = (kk[r >> 2][r & 3] <= qp) ? __builtin_amdgcn_exp2f(sc[r] * p.c2 - lse2) : 0.f;
+          else
+            xp[r] = __builtin_amdgcn_exp2f(fminf(sc[r] * p.c2 - lse2, 0.f));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -980,8 +1003,13 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timer_begin(s);
-  hipLaunchKernelGGL((dq_kernel<DP>), dim3((unsigned)(n_qt * p.B * p.Hq * p.dq_split)), dim3(kBwdThreads), 0, s,
-                     p);
+  {
+    const dim3 grid((unsigned)(n_qt * p.B * p.Hq * p.dq_split));
+    if (p.causal)
+      hipLaunchKernelGGL((dq_kernel<DP, true>), grid, dim3(kBwdThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((dq_kernel<DP, false>), grid, dim3(kBwdThreads), 0, s, p);
+  }
   timer_end(s);
   e = hipGetLastError();
   if (e != hipSuccess || p.dq_split == 1) return e;
