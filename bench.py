@@ -590,8 +590,12 @@ def summarize_pmc(args):
             continue
         b_gui, _ = _per_dispatch(sq, kname, "GRBM_GUI_ACTIVE", reduce="max")
         b_mops, _ = _per_dispatch(sq, kname, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        b_conf, _ = _per_dispatch(sq, kname, "SQ_LDS_BANK_CONFLICT")
+        b_lds, _ = _per_dispatch(sq, kname, "SQ_LDS_IDX_ACTIVE")
         bwd[kname] = {"mfma_busy_pct_of_gui_active": 100.0 * b_busy / (b_gui / 8 * SIMD_NUM) if b_gui else None,
-                      "mfma_bf16_flops_per_launch": b_mops * 512 if b_mops else None, "dispatches_averaged": n_b}
+                      "mfma_bf16_flops_per_launch": b_mops * 512 if b_mops else None,
+                      "lds_bank_conflict_pct_of_lds_active": 100.0 * b_conf / b_lds if b_lds else None,
+                      "dispatches_averaged": n_b}
     if bwd:
         out["backward_kernels"] = bwd
     path = os.path.join(ROOT, "profiles", f"{attn_name}_{w.name}_hbm_traffic.json")
@@ -619,9 +623,9 @@ def _kernel_label(name):
     for k in ("sparse_bits_kernel", "sparse_plan_kernel"):
         if k in name:
             return k
-    m = re.search(r"(dkdv_kernel|dq_kernel)<(\d+)>", name)
+    m = re.search(r"(dkdv_kernel|dq_kernel)<(\d+)(?:, (true|false))?>", name)
     if m:
-        return f"{m.group(1)}<{m.group(2)}>"
+        return f"{m.group(1)}<{m.group(2)}{', causal' if m.group(3) == 'true' else ''}>"
     for k in ("dq_reduce_kernel", "delta_kernel", "bwd_positions_kernel", "merge_kernel", "combine_kernel",
               "upload_kernel", "__amd_rocclr_copyBuffer"):
         if k in name:
