@@ -406,8 +406,9 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
   // i - 1 (query half t = k / (2 NB), column block (k mod 2 NB) / 2, dV for even k) while the vector
   // units turn S(i) and dP(i) into the bf16 words of set C; its last 2 NS slots issue S and dP of
   // block i + 1 (k-step k / 2, S for even k) into the same registers, whose old values are then dead.
-  auto phase = [&](auto c_c, int u) {
+  auto phase = [&](auto c_c, auto m_c, int u) {
     constexpr int C = decltype(c_c)::value, N = C ^ 1;
+    constexpr bool MASKED = decltype(m_c)::value;
     constexpr int NA = 4 * NB;  // slots with vector work
     const QBlock<DP>& cur = ring[u];
     const QBlock<DP>& prv = ring[(u + kRing - 1) % kRing];
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
     auto read_tables = [&](int jj) {
       ls[jj] = *(const f32x4*)(cur.lse2 + 8 * jj + 4 * h);
       de[jj] = *(const f32x4*)(cur.del + 8 * jj + 4 * h);
-      if (CAUSAL) qq[jj] = *(const i32x4*)(cur.qp + 8 * jj + 4 * h);
+      if (MASKED) qq[jj] = *(const i32x4*)(cur.qp + 8 * jj + 4 * h);
     };
     bf16x8 opa[NMF];
     auto read_op = [&](int sl) {
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
         for (int r = 16 * sl / NA; r < 16 * (sl + 1) / NA; ++r) {
           const int jj = r >> 2, e = r & 3;
           xp[r] = __builtin_amdgcn_exp2f(sc[r] * p.c2 - ls[jj][e]);
-          if (CAUSAL) xp[r] = (kp <= qq[jj][e]) ? xp[r] : 0.f;
+          if (MASKED) xp[r] = (kp <= qq[jj][e]) ? xp[r] : 0.f;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -499,7 +500,8 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
   };
 
   // Phases run in pairs until one whose block does not exist: phase n adds dV/dK of the last block
-  // n - 1, and a phase past it adds zeros.
+  // n - 1, and a phase past it adds zeros. MASKED: compare positions for every score.
+  auto walk = [&](auto m_c) {
   int cg = 0, cqb = -1;
   if (advance(cg, cqb)) {
     {
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
         ok3 = true;
         fetch(cg, cqb);  // in flight during the phase
       }
-      phase(c_c, u);
+      phase(c_c, m_c, u);
       __syncthreads();
       u = (u + 1) % kRing;
       const bool real = ok0;
@@ -558,6 +560,19 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
       more = step(BIntC<1>{});
     } while (more);
   }
+  };
+  // A workgroup none of whose query blocks straddles its keys (every visited block sees all of them)
+  // walks without the mask; the test is one pass over the block bounds, shared by the threads.
+  bool need_mask = false;
+  if constexpr (CAUSAL) {
+    for (int qb = tid; qb < n_qb; qb += kBwdThreads)
+      need_mask = need_mask || (p.qblk[2 * qb + 1] >= kmin && p.qblk[2 * qb] < kmax);
+    need_mask = __syncthreads_or(need_mask);
+  }
+  if (need_mask)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
 
   // lane writes its key's row: block db, registers 4i .. 4i+3 are columns db*32 + 8i + 4h .. +3
   if (kvalid) {
