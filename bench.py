@@ -142,8 +142,8 @@ def dominant_kernel(w):
     return "attention_bf16_kernel" if w.dtype == "bf16" else "attention_kernel"
 
 
-def traffic_for(w):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+def counter_summary(w):
+    """The committed rocprofv3 counter summary of a workload, if it matches this source."""
     path = os.path.join(ROOT, "profiles", f"{dominant_kernel(w)}_{w.name}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -151,7 +151,24 @@ def traffic_for(w):
         t = json.load(f)
     if t.get("source_sha256_16") != source_digest():
         return None  # the kernel changed since the counters were taken
-    return t.get("bytes_per_launch")
+    return t
+
+
+def traffic_for(w):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    t = counter_summary(w)
+    return t.get("bytes_per_launch") if t else None
+
+
+def clock_derived_peak(w, achieved):
+    """The bf16 peak at the shader clock the counters saw while the kernel ran (CUs x sclk x 4096
+    flops per clock), from the committed counter summary; the published peak assumes 2.4 GHz."""
+    t = counter_summary(w)
+    if not t or not t.get("sclk_ghz_under_load"):
+        return None
+    peak = t["clock_derived_bf16_peak_tflops"]
+    return {"sclk_ghz": round(t["sclk_ghz_under_load"], 3), "peak": round(peak, 1), "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "source": "GRBM_GUI_ACTIVE over the profiled kernel duration"}
 
 
 def measure_share(w, steps, warmup, settle_s, torch, ra, wl, dev="cuda:0"):
@@ -565,6 +582,9 @@ def summarize_pmc(args):
         "mfma_busy_pct_of_gui_active": 100.0 * busy / (gui * SIMD_NUM) if busy and gui else None,
         "mfma_busy_pct_of_duration_at_2p4ghz": 100.0 * busy / (dur * 2.4e9 * SIMD_NUM) if busy else None,
         "profiled_duration_us": dur * 1e6,
+        # the shader clock while the kernel ran: active cycles of one XCD over the kernel's duration
+        "sclk_ghz_under_load": gui / dur / 1e9 if gui else None,
+        "clock_derived_bf16_peak_tflops": 256 * (gui / dur) * 4096 / 1e12 if gui else None,
         "mfma_bf16_flops_per_launch": mops * 512 if mops else None,
         "counted_flops_per_launch": wl.counted_flops(w),
         "lds_bank_conflict_pct_of_lds_active": 100.0 * conf / lds_act if conf is not None and lds_act else None,
@@ -772,6 +792,7 @@ def main():
             "traffic": traffic_for(w),
         },
         "pct_of_bf16_peak": round(100 * entry["TFLOP/s"] / BF16_PEAK_TFLOPS, 2),
+        "clock_derived_peak": clock_derived_peak(w, entry["kernel_TFLOP/s"]),
         "kernel_source_sha256_16": source_digest(),
     }
 
