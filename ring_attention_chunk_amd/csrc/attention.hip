@@ -1447,13 +1447,23 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
     return min(rel, nvalid - 1) - 4 * h;
   };
   // Keys outside [lo, bound] (both minus 4h) are masked; lo only on block-sparse calls.
+  // The test is lane-local integer arithmetic: the sign of bound - key is spread
+  // over the word and selects the bits of -inf. Written as compares, the 32
+  // results each took a scalar register pair, and the spills of the walk state
+  // this forced ran on every step, masked or not. The empty asm keeps the
+  // compiler from folding the arithmetic back into compares.
   auto mask_tile = [&](f32x16* s, int bound, int lo) {
 #pragma unroll
     for (int k2 = 0; k2 < TB / 32; ++k2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k2 * 32 + 8 * (r >> 2) + (r & 3);
-        if (key > bound || (SP && key < lo)) s[k2][r] = -INFINITY;
+        int hide = (bound - key) >> 31;  // all ones when key > bound
+        if constexpr (SP) hide |= (key - lo) >> 31;
+        asm volatile("" : "+v"(hide));
+        const float sv = s[k2][r];  // copy first: a bit cast of the element itself reads element 0
+        const uint32_t bits = __builtin_bit_cast(uint32_t, sv);
+        s[k2][r] = __builtin_bit_cast(float, (bits & ~(uint32_t)hide) | ((uint32_t)hide & 0xff800000u));
       }
   };
   // Block-sparse calls: the run of keys of the tile starting at position pos0
