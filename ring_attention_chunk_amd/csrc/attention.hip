@@ -192,7 +192,12 @@ struct TileInfo {
   int li;          // block-sparse walk: index of the tile in the work item's list
 };
 
-template <int MODE, int ELEM, int TB = BN, bool SKIP = true>
+// BOUNDS: compute the tile's smallest and largest key position (kmin, kmax)
+// over every chunk it touches. Without BOUNDS (the pipelined kernel, whose
+// tiles are single increasing position progressions) the causal skip tests
+// only the tile's first position, with no loop over chunks: that loop, inlined
+// into every step's successor, slowed the whole causal walk by ~9%.
+template <int MODE, int ELEM, int TB = BN, bool SKIP = true, bool BOUNDS = true>
 __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor, int end, int qmax, int b,
                                               int hk) {
   TileInfo ti;
@@ -207,7 +212,14 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
     }
     int kmin = kPosNone, kmax = kPosMin;
     const bool one = (t1 <= ch.start + ch.len);
-    if (MODE == kRingCausal) {
+    if (MODE == kRingCausal && !BOUNDS) {
+      if (SKIP && ch.pos0 + ch.ps * (int)(t0 - ch.start) > qmax) {
+        // as below: nothing from here to the chunk's end is visible
+        const int nt = (int)((ch.start + ch.len) / TB);
+        t = nt > t ? nt : t + 1;
+        continue;
+      }
+    } else if (MODE == kRingCausal) {
       int c = cursor;
       ChunkDev cc = ch;
       while (true) {
@@ -261,7 +273,7 @@ __device__ __forceinline__ TileInfo next_tile(const Params& p, int t, int cursor
 
 // The tile after `ti` in the walk. When it lies in the same chunk as `ti` (the
 // common case) it follows by scalar arithmetic, with no descriptor load.
-template <int MODE, int ELEM, int TB = BN>
+template <int MODE, int ELEM, int TB = BN, bool BOUNDS = true>
 __device__ __forceinline__ TileInfo successor(const Params& p, const TileInfo& ti, int end, int qmax, int b,
                                               int hk) {
   const int nt = ti.t + 1;
@@ -276,7 +288,7 @@ __device__ __forceinline__ TileInfo successor(const Params& p, const TileInfo& t
     n.vp = ti.vp + (int64_t)TB * ti.ss * ELEM;
     return n;
   }
-  return next_tile<MODE, ELEM, TB>(p, nt, ti.cursor, end, qmax, b, hk);
+  return next_tile<MODE, ELEM, TB, true, BOUNDS>(p, nt, ti.cursor, end, qmax, b, hk);
 }
 
 // Reads of tables the kernels never write, through the constant address space:
@@ -305,22 +317,22 @@ __device__ __forceinline__ int lower_entry(const int* list, int n, int t) {
   return lo;
 }
 
-template <int MODE, int ELEM, int TB = BN>
+template <int MODE, int ELEM, int TB = BN, bool BOUNDS = true>
 __device__ __forceinline__ TileInfo sparse_tile(const Params& p, const SparseWalk& sw, int e, int cursor, int end,
                                                 int qmax, int b, int hk) {
   if (e >= sw.end) {
-    TileInfo ti = next_tile<MODE, ELEM, TB, false>(p, end, cursor, end, qmax, b, hk);
+    TileInfo ti = next_tile<MODE, ELEM, TB, false, BOUNDS>(p, end, cursor, end, qmax, b, hk);
     ti.li = e;
     return ti;
   }
-  TileInfo ti = next_tile<MODE, ELEM, TB, false>(p, cload(sw.list + e), cursor, end, qmax, b, hk);
+  TileInfo ti = next_tile<MODE, ELEM, TB, false, BOUNDS>(p, cload(sw.list + e), cursor, end, qmax, b, hk);
   ti.li = e;
   return ti;
 }
 
 // The entry after `ti`; a tile right after `ti` in the same chunk follows by
 // scalar arithmetic, as in the dense walk.
-template <int MODE, int ELEM, int TB = BN>
+template <int MODE, int ELEM, int TB = BN, bool BOUNDS = true>
 __device__ __forceinline__ TileInfo sparse_successor(const Params& p, const SparseWalk& sw, const TileInfo& ti,
                                                      int end, int qmax, int b, int hk) {
   const int e = ti.li + 1;
@@ -338,7 +350,7 @@ __device__ __forceinline__ TileInfo sparse_successor(const Params& p, const Spar
       return n;
     }
   }
-  return sparse_tile<MODE, ELEM, TB>(p, sw, e, ti.cursor, end, qmax, b, hk);
+  return sparse_tile<MODE, ELEM, TB, BOUNDS>(p, sw, e, ti.cursor, end, qmax, b, hk);
 }
 
 // Key and value row addresses and position of tile row r; false past the last key.
@@ -1533,12 +1545,12 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
   }
   auto next_of = [&](const TileInfo& x) {
     if constexpr (SP)
-      return uniform(sparse_successor<MODE, 2, TB>(p, sw, x, tend, wk.gqmax, b, hk));
+      return uniform(sparse_successor<MODE, 2, TB, false>(p, sw, x, tend, wk.gqmax, b, hk));
     else
-      return uniform(successor<MODE, 2, TB>(p, x, tend, wk.gqmax, b, hk));
+      return uniform(successor<MODE, 2, TB, false>(p, x, tend, wk.gqmax, b, hk));
   };
-  const TileInfo t0 = SP ? uniform(sparse_tile<MODE, 2, TB>(p, sw, e0, 0, tend, wk.gqmax, b, hk))
-                         : uniform(next_tile<MODE, 2, TB>(p, tbeg, 0, tend, wk.gqmax, b, hk));
+  const TileInfo t0 = SP ? uniform(sparse_tile<MODE, 2, TB, false>(p, sw, e0, 0, tend, wk.gqmax, b, hk))
+                         : uniform(next_tile<MODE, 2, TB, true, false>(p, tbeg, 0, tend, wk.gqmax, b, hk));
   if (t0.t < tend) {
     f32x16 sa[TB / 32], sb[TB / 32];
     // Tile index and first position of tiles j .. j+D, in slot (tile mod NB),
