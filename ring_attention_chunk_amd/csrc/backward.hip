@@ -61,6 +61,13 @@ constexpr int kPosAllQ = 0x7ffffffe;         // query position that sees every r
 constexpr int kPosMinQ = -0x7fffffff - 1;    // position of a missing query row: sees nothing
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Workgroups are dealt to the 8 XCDs round-robin; when the grid is a multiple of
+// 8, renumber them so that each XCD takes one contiguous range of work items and
+// the items running together on an XCD share that XCD's L2.
+__device__ __forceinline__ int xcd_item(int blk, int nwg) {
+  return (nwg & 7) == 0 ? (blk & 7) * (nwg >> 3) + (blk >> 3) : blk;
+}
+
 struct BwdChunk {
   const void* k;
   const void* v;
@@ -298,8 +305,11 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const typename T::Lanes LL = T::lanes(lane);
   const int n_kt = (int)((p.Lk + kGroupRows - 1) / kGroupRows);
-  const int kt = blockIdx.x % n_kt;
-  const int bh = blockIdx.x / n_kt;
+  // causal: the renumbering below measured +10-40% on causal shares (unequal work per item)
+  // and -1% on the non-causal long GQA share, which keeps the plain order
+  const int item = CAUSAL ? xcd_item(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int kt = item % n_kt;
+  const int bh = item / n_kt;
   const int hk = bh % p.Hkv, b = bh / p.Hkv;
   const int group = p.Hq / p.Hkv;
 
@@ -629,8 +639,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const typename T::Lanes LL = T::lanes(lane);
   const int n_qt = (int)((p.Lq + kGroupRows - 1) / kGroupRows);
-  const int qt = blockIdx.x % n_qt;
-  const int rest = blockIdx.x / n_qt;
+  const int item = CAUSAL ? xcd_item(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  // causal: later queries see more keys, so their tiles start first
+  const int qt = CAUSAL ? n_qt - 1 - item % n_qt : item % n_qt;
+  const int rest = item / n_qt;
   const int bh = rest % (p.B * p.Hq), split = rest / (p.B * p.Hq);
   const int hq = bh % p.Hq, b = bh / p.Hq;
   const int hk = hq / (p.Hq / p.Hkv);
