@@ -121,11 +121,26 @@ __device__ __forceinline__ BwdChunk chunk_at(const BwdChunk* chunks, int i) {
 typedef const __attribute__((address_space(4))) int* cint_ptr;
 __device__ __forceinline__ int cload(const int* p) { return *(cint_ptr)p; }
 
+// Per-lane reads of the chunk table and of key rows through the global address
+// space. Through a generic pointer they would be flat loads, which count on the
+// LDS wait counter as well: one in a loop makes the compiler wait for every
+// outstanding LDS read (lgkmcnt(0)) wherever the loop waits for one.
+typedef const __attribute__((address_space(1))) BwdChunk* gchunk_ptr;
+typedef const __attribute__((address_space(1))) u32x4* gu32x4_ptr;
+__device__ __forceinline__ u32x4 gload16(const void* ptr) { return *(gu32x4_ptr)ptr; }
+
 // Row address of key j (chunk `c` holds it); the cursor only moves forward.
 __device__ __forceinline__ int64_t key_offset(const BwdParams& p, int64_t j, int b, int hk, int& c) {
-  while (c + 1 < p.n_chunks && j >= p.chunks[c].start + p.chunks[c].len) ++c;
-  const BwdChunk& ch = p.chunks[c];
-  return (int64_t)b * ch.sb + (int64_t)hk * ch.sh + (j - ch.start) * ch.ss;
+  const gchunk_ptr chunks = (gchunk_ptr)p.chunks;
+  while (c + 1 < p.n_chunks && j >= chunks[c].start + chunks[c].len) ++c;
+  return (int64_t)b * chunks[c].sb + (int64_t)hk * chunks[c].sh + (j - chunks[c].start) * chunks[c].ss;
+}
+// Key pointer of chunk c.
+__device__ __forceinline__ const __bf16* chunk_k(const BwdParams& p, int c) {
+  return (const __bf16*)((gchunk_ptr)p.chunks)[c].k;
+}
+__device__ __forceinline__ const __bf16* chunk_v(const BwdParams& p, int c) {
+  return (const __bf16*)((gchunk_ptr)p.chunks)[c].v;
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& x, int t) {
@@ -321,15 +336,15 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
   {
     int c = 0;
     const int64_t off = kvalid ? key_offset(p, j, b, hk, c) : 0;
-    const __bf16* kr = (const __bf16*)p.chunks[c].k + off;
-    const __bf16* vr = (const __bf16*)p.chunks[c].v + off;
+    const __bf16* kr = chunk_k(p, c) + off;
+    const __bf16* vr = chunk_v(p, c) + off;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int col = 16 * s + 8 * h;
       u32x4 kraw = {0u, 0u, 0u, 0u}, vraw = {0u, 0u, 0u, 0u};
       if (kvalid && col < p.d) {
-        kraw = *(const u32x4*)(kr + col);
-        vraw = *(const u32x4*)(vr + col);
+        kraw = gload16(kr + col);
+        vraw = gload16(vr + col);
       }
       kf[s] = __builtin_bit_cast(bf16x8, kraw);
       vf[s] = __builtin_bit_cast(bf16x8, vraw);
@@ -723,8 +738,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
         } else {
           cur[k] = max(cur[k], cc);
           const int64_t off = key_offset(p, j0 + r, b, hk, cur[k]);
-          pk[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].k + off + c8 * 8);
-          pv[k] = *(const u32x4*)((const __bf16*)p.chunks[cur[k]].v + off + c8 * 8);
+          pk[k] = gload16(chunk_k(p, cur[k]) + off + c8 * 8);
+          pv[k] = gload16(chunk_v(p, cur[k]) + off + c8 * 8);
         }
       }
     }
