@@ -1460,10 +1460,11 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
   };
   // Keys outside [lo, bound] (both minus 4h) are masked; lo only on block-sparse calls.
   // The test is lane-local integer arithmetic: the sign of bound - key is spread
-  // over the word and selects the bits of -inf. Written as compares, the 32
-  // results each took a scalar register pair, and the spills of the walk state
-  // this forced ran on every step, masked or not. The empty asm keeps the
-  // compiler from folding the arithmetic back into compares.
+  // over the word and selects the bits of -inf. Written as compares, every
+  // element's result took a scalar register pair, and the spills of the walk
+  // state this forced ran on every step, masked or not. The empty asm keeps the
+  // compiler from turning the selects back into compares whose results it holds
+  // in scalar registers.
   auto mask_tile = [&](f32x16* s, int bound, int lo) {
 #pragma unroll
     for (int k2 = 0; k2 < TB / 32; ++k2)
