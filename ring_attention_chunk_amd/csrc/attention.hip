@@ -165,12 +165,27 @@ __device__ __forceinline__ u32x4 gload16(const void* ptr) { return *(gptr_u32x4)
 __device__ __forceinline__ uint32_t gload_u16(const void* ptr) { return *(gptr_u16)ptr; }
 __device__ __forceinline__ float gload_f32(const void* ptr) { return *(gptr_f32)ptr; }
 
+// Chunk descriptors are read through the constant address space: with the
+// walk's uniform cursor these are scalar loads, which leave the vector memory
+// counter (that the LDS copy pipeline waits on) alone.
+typedef const __attribute__((address_space(4))) ChunkDev* cchunk_ptr;
 template <int MODE>
 __device__ __forceinline__ ChunkDev chunk_at(const Params& p, int c) {
   if constexpr (MODE == kStats) {
     return p.one;
   } else {
-    return p.chunks[c];
+    const cchunk_ptr x = (cchunk_ptr)p.chunks + c;
+    ChunkDev r;  // field by field: no copy constructor takes a constant-address-space source
+    r.k = x->k;
+    r.v = x->v;
+    r.start = x->start;
+    r.len = x->len;
+    r.sb = x->sb;
+    r.sh = x->sh;
+    r.ss = x->ss;
+    r.pos0 = x->pos0;
+    r.ps = x->ps;
+    return r;
   }
 }
 
