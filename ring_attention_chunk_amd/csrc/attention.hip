@@ -1613,7 +1613,7 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
     // The four ring buffers of a step are passed as restrict pointers: the
     // compiler then knows that the reads of K(j+1) and V(j) do not touch the
     // buffers being filled, and does not make them wait for those copies.
-    auto step_body = [&](f32x16* sc, f32x16* sn, auto bi_c, auto mask_c, int bound, int lo, bool lo_any,
+    auto step_body = [&](f32x16* sc, f32x16* sn, auto bi_c, auto mask_c, bool need, int tn, int pn, int mrun,
                          char* __restrict__ k_fill, char* __restrict__ v_fill, const char* __restrict__ k_read,
                          const char* __restrict__ v_read) {
       constexpr int BI = decltype(bi_c)::value;
@@ -1633,10 +1633,14 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
       __builtin_amdgcn_s_setprio(1);
       fused(k_read, v_read, sc, sn, mt);
       __builtin_amdgcn_s_setprio(0);
-      // some lane of the wave cannot see every key of tile j+1 (its highest key
-      // index in a lane is TB - 5 + 4h): mask, and take the maximum again (the
-      // masked maximum never exceeds the one above)
-      if (MASKED && (__any(bound < TB - 5) || (SP && lo_any))) {
+      // some lane of the wave may not see every key of tile j+1: mask, and take
+      // the maximum again (the masked maximum never exceeds the one above)
+      if (MASKED && need) {
+        int bound = key_bound(tn, pn), lo = 0;
+        if constexpr (SP) {
+          bound = min(bound, (mrun & 0xffff) - 1 - 4 * h);
+          lo = (mrun >> 16) - 4 * h;
+        }
         mask_tile(sn, bound, lo);
         mt = fminf(mt, lane_max(sn));
       }
@@ -1645,17 +1649,24 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
     };
     auto step = [&](f32x16* sc, f32x16* sn, auto bi_c) {
       constexpr int BI = decltype(bi_c)::value;
-      int bound = MASK ? key_bound(qt[(BI + 1) % NB], qp[(BI + 1) % NB]) : 0;
-      int lo = 0;
-      bool lo_any = false;
-      if constexpr (SP) {
-        const int m = qm[(BI + 1) % NB];
-        bound = min(bound, (m & 0xffff) - 1 - 4 * h);
-        lo = (m >> 16) - 4 * h;
-        lo_any = (m >> 16) > 0;
+      const int tn = qt[(BI + 1) % NB], pn = qp[(BI + 1) % NB];
+      // A uniform test (scalar work) of whether some lane of the wave may not see every key of tile
+      // j+1: a ragged last tile, or the wave's earliest query before the tile's last key (key i sits
+      // at pos0 + kps i). It may say yes where every lane sees every key, never the reverse; the
+      // per-lane bound is formed only then.
+      bool need = false;
+      int mrun = 0;
+      if constexpr (MASK) {
+        const int64_t nvalid = min((int64_t)TB, p.Lk - (int64_t)tn * TB);
+        need = nvalid < TB || (int64_t)wk.wqmin - pn < (int64_t)p.kps * (TB - 1);
       }
-      step_body(sc, sn, bi_c, IntC<MASK>{}, bound, lo, lo_any, kbuf[BI], vbuf[(BI + D) % NB], kbuf[(BI + 1) % NB],
-                vbuf[BI]);
+      if constexpr (SP) {
+        // the block mask's run of admitted keys: anything short of the whole tile needs the mask
+        mrun = qm[(BI + 1) % NB];
+        need = need || (mrun >> 16) > 0 || (mrun & 0xffff) < TB;
+      }
+      step_body(sc, sn, bi_c, IntC<MASK>{}, need, tn, pn, mrun, kbuf[BI], vbuf[(BI + D) % NB],
+                kbuf[(BI + 1) % NB], vbuf[BI]);
     };
 
     while (true) {
