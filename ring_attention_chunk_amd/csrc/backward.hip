@@ -431,10 +431,12 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
   // i - 1 (query half t = k / (2 NB), column block (k mod 2 NB) / 2, dV for even k) while the vector
   // units turn S(i) and dP(i) into the bf16 words of set C; its last 2 NS slots issue S and dP of
   // block i + 1 (k-step k / 2, S for even k) into the same registers, whose old values are then dead.
-  auto phase = [&](auto c_c, auto m_c, int u) {
+  auto phase = [&](auto c_c, auto m_c, auto u_c) {
     constexpr int C = decltype(c_c)::value, N = C ^ 1;
     constexpr bool MASKED = decltype(m_c)::value;
     constexpr int NA = 4 * NB;  // slots with vector work
+    constexpr int u = decltype(u_c)::value;  // ring slot of block i: a constant, so that operand
+                                             // addresses fold the slot into the instruction offset
     const QBlock<DP>& cur = ring[u];
     const QBlock<DP>& prv = ring[(u + kRing - 1) % kRing];
     const QBlock<DP>& nxt = ring[(u + 1) % kRing];
@@ -559,8 +561,8 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
 #pragma unroll
       for (int w = 0; w < 4; ++w) pw[1][t][w] = dw[1][t][w] = 0u;
 
-    int u = 0;  // ring slot of block i
-    auto step = [&](auto c_c) {
+    auto step = [&](auto c_c, auto u_c) {  // u_c: ring slot of block i
+      constexpr int u = decltype(u_c)::value;
       if (ok2)
         put(ring[(u + 2) % kRing]);
       else
@@ -570,19 +572,22 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
         ok3 = true;
         fetch(cg, cqb);  // in flight during the phase
       }
-      phase(c_c, m_c, u);
+      phase(c_c, m_c, u_c);
       __syncthreads();
-      u = (u + 1) % kRing;
       const bool real = ok0;
       ok0 = ok1;
       ok1 = ok2;
       ok2 = ok3;
       return real;
     };
+    // four steps per iteration (one per ring slot), leaving the loop only after the fourth: a walk
+    // ends with up to four phases over blocks that do not exist, which add zeros
     bool more;
     do {
-      step(BIntC<0>{});
-      more = step(BIntC<1>{});
+      step(BIntC<0>{}, BIntC<0>{});
+      step(BIntC<1>{}, BIntC<1>{});
+      step(BIntC<0>{}, BIntC<2>{});
+      more = step(BIntC<1>{}, BIntC<3>{});
     } while (more);
   }
   };
