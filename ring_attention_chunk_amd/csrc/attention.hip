@@ -1350,7 +1350,6 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
   constexpr int kRA = 2;               // slots between an LDS read and its use
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   auto fused = [&](const char* __restrict__ k_read, const char* __restrict__ v_read, const f32x16* sc, f32x16* sn,
                    float& mt_out) {
     bf16x8 ka[NSL], va[NSL];
@@ -1368,7 +1367,6 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
         va[sl] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float rs0 = 0.f, rs1 = 0.f;
     float mx[NG][2];
 #pragma unroll
@@ -1388,16 +1386,18 @@ __global__ __launch_bounds__(64 * pipe_waves(MODE), pipe_resident(MODE)) void at
         xv[2 * w] = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + t], c2, -ms));
         xv[2 * w + 1] = __builtin_amdgcn_exp2f(fmaf(sc[ks >> 1][(ks & 1) * 8 + t + 1], c2, -ms));
       };
-      auto pack = [&](int w) {  // bf16 pair and its row sum
+      // bf16 pair for P.V, and the row sum of the fp32 values. The sum is two
+      // plain adds: v_dot2_f32_bf16 on the packed pair, one instruction instead
+      // of two, stalls the matrix unit when issued between MFMAs (measured on
+      // this chip: one per MFMA slows a stream of MFMAs by 50-70%)
+      auto pack = [&](int w) {
         const int t = part * VPS + 2 * w;
         typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
         const bf16x2v pr = {(__bf16)xv[2 * w], (__bf16)xv[2 * w + 1]};
         const uint32_t word = __builtin_bit_cast(uint32_t, pr);
         pw[ks][t / 2] = word;
-        if ((t / 2) & 1)
-          rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, rs1, false);
-        else
-          rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, rs0, false);
+        rs0 += xv[2 * w];
+        rs1 += xv[2 * w + 1];
       };
       constexpr int WPS = VPS / 2, WA = (WPS + 1) / 2;  // words per slot, words in the first half
       if (sl < NM) {
