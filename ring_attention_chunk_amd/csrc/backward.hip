@@ -777,8 +777,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
   // One phase (tile i in ring slot u): NA slots of dQ products of tile i - 1 (key half t = k / NB,
   // column block k mod NB) with the vector work on S(i), dP(i), then 2 NS slots of S and dP of tile
   // i + 1 (k-step k / 2, S for even k) into the same registers.
-  auto phase = [&](auto c_c, int u) {
+  auto phase = [&](auto c_c, auto u_c) {
     constexpr int C = decltype(c_c)::value, N = C ^ 1;
+    constexpr int u = decltype(u_c)::value;  // ring slot of tile i: a constant, as in the dK/dV kernel
     const KTile<DP>& cur_t = ring[u];
     const KTile<DP>& prv = ring[(u + kRing - 1) % kRing];
     const KTile<DP>& nxt = ring[(u + 1) % kRing];
@@ -843,8 +844,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
     }
   };
 
-  // Phases run in pairs until one whose tile does not exist: phase n adds dQ of the last tile n - 1,
-  // and a phase past it adds zeros.
+  // Phases run four at a time until one whose tile does not exist: phase n adds dQ of the last tile
+  // n - 1, and phases past it add zeros.
   int t = t_beg - 1;
   if (advance(t)) {
     {
@@ -877,8 +878,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) dw[1][tt][w] = 0u;
 
-    int u = 0;  // ring slot of tile i
-    auto step = [&](auto c_c) {
+    auto step = [&](auto c_c, auto u_c) {  // u_c: ring slot of tile i
+      constexpr int u = decltype(u_c)::value;
       if (ok2)
         put(ring[(u + 2) % kRing]);
       else
@@ -888,19 +889,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void dq_kernel(BwdParams p) {
         ok3 = true;
         fetch(t);  // in flight during the phase
       }
-      phase(c_c, u);
+      phase(c_c, u_c);
       __syncthreads();
-      u = (u + 1) % kRing;
       const bool real = ok0;
       ok0 = ok1;
       ok1 = ok2;
       ok2 = ok3;
       return real;
     };
+    // four steps per iteration, one per ring slot (up to four trailing phases add zeros)
     bool more;
     do {
-      step(BIntC<0>{});
-      more = step(BIntC<1>{});
+      step(BIntC<0>{}, BIntC<0>{});
+      step(BIntC<1>{}, BIntC<1>{});
+      step(BIntC<0>{}, BIntC<2>{});
+      more = step(BIntC<1>{}, BIntC<3>{});
     } while (more);
   }
 
