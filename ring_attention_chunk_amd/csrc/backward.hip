@@ -526,8 +526,8 @@ __global__ __launch_bounds__(kBwdThreads, dkdv_resident(DP)) void dkdv_kernel(Bw
     }
   };
 
-  // Phases run in pairs until one whose block does not exist: phase n adds dV/dK of the last block
-  // n - 1, and a phase past it adds zeros. MASKED: compare positions for every score.
+  // Phases run four at a time until one whose block does not exist: phase n adds dV/dK of the last
+  // block n - 1, and phases past it add zeros. MASKED: compare positions for every score.
   auto walk = [&](auto m_c) {
   int cg = 0, cqb = -1;
   if (advance(cg, cqb)) {
