@@ -1788,18 +1788,23 @@ __global__ __launch_bounds__(256) void merge_kernel(int64_t rows, int d, int lpr
       fa = expf(ma - mx);
       fb = expf(mb - mx);
     }
+    // every byte of u is touched once: non-temporal loads and stores keep the
+    // stream out of the caches (+16% on 1.6 GB of rotating statistics, where the
+    // plain accesses ran at a device copy's rate)
     if (VEC4) {
       const int n4 = d >> 2;
       f32x4* pa = (f32x4*)(au + r * d);
       const f32x4* pb = (const f32x4*)(bu + r * d);
       for (int c = sub; c < n4; c += lpr) {
-        const f32x4 x = pa[c], y = pb[c];
-        pa[c] = x * fa + y * fb;
+        const f32x4 x = __builtin_nontemporal_load(pa + c), y = __builtin_nontemporal_load(pb + c);
+        __builtin_nontemporal_store(x * fa + y * fb, pa + c);
       }
     } else {
       float* pa = au + r * d;
       const float* pb = bu + r * d;
-      for (int c = sub; c < d; c += lpr) pa[c] = pa[c] * fa + pb[c] * fb;
+      for (int c = sub; c < d; c += lpr)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(pa + c) * fa + __builtin_nontemporal_load(pb + c) * fb,
+                                    pa + c);
     }
     if (sub == 0) {
       am[r] = mx;
