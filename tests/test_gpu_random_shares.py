@@ -76,7 +76,8 @@ def _check(got, ref, dtype):
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
 
 
-@pytest.mark.parametrize("seed", range(N_CASES))
+# seed 592: one query that sees one key, so its exact dq and dk are zero
+@pytest.mark.parametrize("seed", list(range(N_CASES)) + [592])
 def test_random_share(seed):
     w = _case(seed)
     print(f"[case] {w.name} B={w.batch} Hq={w.q_heads} Hkv={w.kv_heads} q={w.q_segments} chunks={w.chunks}",
@@ -107,5 +108,11 @@ def test_random_share(seed):
         want = gref[name]
         e = np.abs(got - want)
         assert np.all(np.isfinite(got)), name
+        if not np.any(want):
+            # every query that sees a key sees exactly one: its weight is 1 and dS = P (dP - delta) is exactly
+            # 0, so dq and dk are 0; the kernels leave the fp32 rounding of dP - delta (dP from the bf16
+            # products, delta from out, which is v to fp32 rounding), orders below any real gradient
+            assert e.max() <= 2.0 ** -16, (name, e.max())
+            continue
         assert e.max() <= 1e-2 * max(np.abs(want).max(), 1e-6), (name, e.max(), np.abs(want).max())
         assert e.mean() <= 5e-3 * max(np.abs(want).mean(), 1e-6), (name, e.mean(), np.abs(want).mean())
